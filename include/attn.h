@@ -1,0 +1,138 @@
+/*
+ * attn.h -- C ABI of libattn.so: exact scaled dot-product attention on MI355X
+ * (gfx950), computed as one fused tiled kernel per call that never writes the
+ * score matrix to device memory.
+ *
+ * The operation (pages cited by title and section):
+ *   "Transformer 架构的数学与计算深度解析：注意力机制的详尽研究报告", sec. 2.2-2.4:
+ *     S = scale * Q K^T, A = row softmax(S), O = A V (rows of A sum to one);
+ *     sec. 4.1: the causal mask removes future keys (weight exactly zero);
+ *     sec. 6.3: the online-softmax recurrence that lets the kernel stream K/V
+ *     tiles while keeping only a running max, a denominator and an
+ *     accumulator per query row.
+ *   "从注意力到 IO 感知执行" (auturnal.com review), sec. 8, eqs. (1)-(2): the
+ *     same recurrence with the un-normalised accumulator u and o = u / l.
+ *   pwwt.cn engineering blog on Transformer algorithm evolution, sec. 2.3:
+ *     grouped-query attention, where consecutive query heads share a K/V head.
+ *   "Transformer 笔记：注意力机制为什么会变成系统问题" (imreese.github.io),
+ *     KV-cache section: a decode step's single query reads the cached K/V.
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing and keeps no mutable global state; calls on different
+ *     streams may run concurrently.
+ *   - Tensors are contiguous, row-major, head dim innermost, 16-byte aligned
+ *     (lse and seq_lens: 4-byte aligned).
+ *   - Calls are asynchronous on `stream` (NULL = the null stream) and return
+ *     after the launch is enqueued.
+ *   - Arguments are validated before any HIP runtime call; an invalid call
+ *     returns a non-zero status and enqueues nothing.  No C++ exception
+ *     crosses this interface.
+ *   - LSE is the natural-log log-sum-exp of each row's visible scaled scores,
+ *     fp32; a row that sees no key has O = 0 and LSE = -inf.
+ */
+#ifndef EXACT_SDPA_ATTN_H
+#define EXACT_SDPA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The HIP stream handle type (same declaration as hip_runtime_api.h). */
+typedef struct ihipStream_t *hipStream_t;
+
+/* Element type of q, k, v, o (and of the caches for decode). */
+enum { ATTN_F32 = 0, ATTN_BF16 = 1 };
+
+/* Status codes. */
+enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, non-finite scale */
+    ATTN_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. d not 64/128) */
+    ATTN_ERR_WORKSPACE = 3,   /* decode workspace missing or too small */
+    ATTN_ERR_LAUNCH = 4       /* the HIP runtime reported an error at launch */
+};
+
+/*
+ * attn_fwd -- prefill / self- or cross-attention forward, MHA or GQA.
+ *
+ *   q   [B, Hq,  Nq, d]   dtype          (read)
+ *   k   [B, Hkv, Nk, d]   dtype          (read)
+ *   v   [B, Hkv, Nk, d]   dtype          (read)
+ *   o   [B, Hq,  Nq, d]   dtype          (written; bf16 is rounded to nearest even)
+ *   lse [B, Hq,  Nq]      fp32 or NULL   (written when non-NULL)
+ *
+ * Query head h uses K/V head h / (Hq / Hkv) (contiguous groups).
+ * scale multiplies q.k before masking and the softmax (1/sqrt(d) in the
+ * usual case; any finite value is accepted).
+ * causal != 0 masks key j for query row i when j > i + (Nk - Nq): the query
+ * block is aligned with the END of the key sequence, so the last query row
+ * sees every key (chunked prefill and decode agree with full causal prefill).
+ * causal requires Nq <= Nk.
+ *
+ * Sizes: B >= 0, Nq >= 0, Nk >= 0, Hq >= 1, Hkv >= 1, Hq % Hkv == 0,
+ * d in {64, 128}.  B == 0 or Nq == 0 is a no-op; Nk == 0 (non-causal) gives
+ * O = 0 and LSE = -inf.  dtype is ATTN_F32 or ATTN_BF16; accumulation is fp32
+ * in both cases.
+ *
+ * Returns ATTN_OK, or ATTN_ERR_INVALID_ARG / ATTN_ERR_UNSUPPORTED (nothing
+ * launched), or ATTN_ERR_LAUNCH.
+ */
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+             int causal, int dtype, hipStream_t stream);
+
+/*
+ * attn_decode_workspace_bytes -- bytes of device workspace attn_decode needs
+ * for these sizes: fp32 partial outputs and partial LSEs of every
+ * (sequence, query head, key split).  keys_per_split as for attn_decode
+ * (0 = library default).  Returns 0 for invalid sizes.
+ */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_seq_len,
+                                   int d, int keys_per_split);
+
+/*
+ * attn_decode -- one decode step per sequence against a KV cache (split-KV).
+ *
+ *   q        [B, Hq, d]                 dtype (read): the new token's queries
+ *   k_cache  [B, Hkv, max_seq_len, d]   dtype (read)
+ *   v_cache  [B, Hkv, max_seq_len, d]   dtype (read)
+ *   seq_lens [B] int32, device          (read): rows 0..seq_lens[b]-1 of
+ *            sequence b are valid; values are clamped to [0, max_seq_len].
+ *            Rows at or beyond seq_lens[b] are never read.
+ *   o        [B, Hq, d]                 dtype (written)
+ *   lse      [B, Hq] fp32 or NULL       (written when non-NULL)
+ *   workspace / workspace_bytes: caller-owned device scratch of at least
+ *            attn_decode_workspace_bytes(...) bytes, 16-byte aligned; its
+ *            contents on entry do not matter.  Two calls that overlap in time
+ *            must not share one workspace.
+ *
+ * Query head h of sequence b attends, without a mask, to the first
+ * seq_lens[b] rows of K/V head h / (Hq / Hkv); this equals the last row of
+ * causal attn_fwd over those rows.  The cache is not appended to.
+ * The keys of each (b, K/V head) are cut into splits of keys_per_split rows
+ * (0 = default 256; otherwise a multiple of 64 in [64, 65536]); each split
+ * produces a partial result that a second kernel merges through the partial
+ * log-sum-exps.  Only dtype ATTN_BF16 is implemented; Hq / Hkv must be at
+ * most 16.
+ *
+ * Sizes: B >= 0 (0 is a no-op), Hq >= 1, Hkv >= 1, Hq % Hkv == 0,
+ * max_seq_len >= 0, d in {64, 128}.
+ */
+int attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                const int32_t *seq_lens, void *o, float *lse, int B, int Hq,
+                int Hkv, int max_seq_len, int d, float scale,
+                int keys_per_split, int dtype, void *workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *attn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_SDPA_ATTN_H */

@@ -1,0 +1,367 @@
+"""Pins of the fp64 oracle to facts fixed by the pages and by mathematics.
+
+Each pin takes an ``oracle.Oracle`` and raises AssertionError when the oracle
+disagrees with something independent of the oracle's own code: a
+high-precision brute force of the definition, a library routine
+(torch's CPU scaled_dot_product_attention and logsumexp in fp64), a closed
+form, or an invariant the pages state.  ``tests/test_oracle_mutants.py`` runs
+every pin against deliberately broken copies of the oracle to show that each
+plausible mistake is caught by at least one pin.
+
+Pages (cited by title and section):
+  [R]  "Transformer 架构的数学与计算深度解析：注意力机制的详尽研究报告":
+       sec. 2.4 (rows of weights sum to one; output is a convex combination of
+       value rows), sec. 4.1 (causal: token t sees positions 1..t),
+       sec. 6.3 (the online recurrence reaches exactly the standard result).
+  [IO] "从注意力到 IO 感知执行": sec. 8 (subtracting the max leaves the
+       probabilities unchanged; recurrence eqs. (1)-(2)).
+  [N]  "Transformer 笔记：注意力机制为什么会变成系统问题": KV-cache section
+       (a decode query reads the cached K/V of all earlier tokens).
+  [E]  pwwt.cn engineering blog: sec. 2.3 (GQA: a group of query heads shares
+       one K/V head), sec. 5.1 (attention is order-insensitive: shuffling the
+       sequence only shuffles the output).
+"""
+from decimal import Decimal, getcontext
+
+import numpy as np
+import torch
+
+TOL = 1e-12
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _randn(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, "%s: shape %s vs %s" % (what, a.shape, b.shape)
+    both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    diff = np.where(both_inf, 0.0, np.abs(a - b))
+    err = float(np.nanmax(diff)) if diff.size else 0.0
+    assert not np.isnan(diff).any(), "%s: NaN" % what
+    assert err <= tol, "%s: max abs err %.3e > %.1e" % (what, err, tol)
+
+
+# ---------------------------------------------------------------------------
+# 1. brute force in 50-digit decimal arithmetic, softmax written as
+#    exp(s_j) / sum_k exp(s_k) with no max subtraction ([R] sec. 2.4).
+# ---------------------------------------------------------------------------
+def _decimal_attention(q, k, v, scale, causal):
+    getcontext().prec = 50
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    o = np.zeros(q.shape)
+    lse = np.zeros(q.shape[:3])
+    sc = Decimal(repr(float(scale)))
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // G
+            for i in range(Nq):
+                es = []
+                for j in range(Nk):
+                    if causal and j > i:  # square case only: token i sees 0..i
+                        continue
+                    s = sum(Decimal(repr(float(q[b, h, i, c]))) * Decimal(repr(float(k[b, hk, j, c])))
+                            for c in range(d)) * sc
+                    es.append((j, s.exp()))
+                z = sum(e for _, e in es)
+                for c in range(d):
+                    acc = sum(e * Decimal(repr(float(v[b, hk, j, c]))) for j, e in es)
+                    o[b, h, i, c] = float(acc / z)
+                lse[b, h, i] = float(z.ln())
+    return o, lse
+
+
+def pin_decimal_bruteforce(orc):
+    rng = _rng(1)
+    cases = [
+        (2, 4, 2, 5, 7, 3, False),   # GQA, rectangular (cross-attention shape)
+        (1, 2, 1, 6, 6, 4, True),    # GQA, causal square
+        (1, 3, 3, 4, 2, 2, False),   # Nq > Nk, non-causal
+        (1, 1, 1, 1, 1, 5, True),    # single token
+    ]
+    for (B, Hq, Hkv, Nq, Nk, d, causal) in cases:
+        q = _randn(rng, B, Hq, Nq, d)
+        k = _randn(rng, B, Hkv, Nk, d)
+        v = _randn(rng, B, Hkv, Nk, d)
+        scale = 1.0 / np.sqrt(d)
+        o, lse = orc.attn(q, k, v, scale, causal)
+        o_ref, lse_ref = _decimal_attention(q, k, v, scale, causal)
+        _close(o, o_ref, TOL, "decimal brute force O %s" % ((B, Hq, Hkv, Nq, Nk, d, causal),))
+        _close(lse, lse_ref, TOL, "decimal brute force LSE")
+
+
+# ---------------------------------------------------------------------------
+# 2. library special case: torch's CPU SDPA and logsumexp in fp64.
+# ---------------------------------------------------------------------------
+def _torch_ref(q, k, v, scale, causal):
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x)) for x in (q, k, v))
+    G = q.shape[1] // k.shape[1]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, scale=scale, is_causal=causal, enable_gqa=(G > 1))
+    kk = tk.repeat_interleave(G, dim=1)
+    s = (tq @ kk.transpose(-1, -2)) * scale
+    if causal:
+        Nq, Nk = s.shape[-2], s.shape[-1]
+        mask = torch.ones(Nq, Nk, dtype=torch.bool).triu(1)
+        s = s.masked_fill(mask, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    return o.numpy(), lse.numpy()
+
+
+def pin_torch_sdpa(orc):
+    rng = _rng(2)
+    cases = [
+        (1, 1, 1, 128, 128, 64, False),
+        (1, 1, 1, 128, 128, 64, True),
+        (2, 8, 2, 33, 33, 16, True),   # GQA, causal, square
+        (2, 6, 3, 17, 40, 8, False),   # GQA, cross-attention (Nq != Nk)
+    ]
+    for (B, Hq, Hkv, Nq, Nk, d, causal) in cases:
+        q = _randn(rng, B, Hq, Nq, d)
+        k = _randn(rng, B, Hkv, Nk, d)
+        v = _randn(rng, B, Hkv, Nk, d)
+        scale = 1.0 / np.sqrt(d)
+        o, lse = orc.attn(q, k, v, scale, causal)
+        o_ref, lse_ref = _torch_ref(q, k, v, scale, causal)
+        _close(o, o_ref, 1e-11, "torch SDPA O %s" % ((B, Hq, Hkv, Nq, Nk, d, causal),))
+        _close(lse, lse_ref, 1e-11, "torch logsumexp LSE")
+
+
+# ---------------------------------------------------------------------------
+# 3. invariants and closed forms ([R] sec. 2.4, 4.1; [IO] sec. 8)
+# ---------------------------------------------------------------------------
+def pin_rows_sum_to_one(orc):
+    rng = _rng(3)
+    for causal in (False, True):
+        q = _randn(rng, 1, 2, 24, 8)
+        k = _randn(rng, 1, 2, 24, 8)
+        v = _randn(rng, 1, 2, 24, 8)
+        o, lse, w = orc.attn(q, k, v, 0.35, causal, weights=True)
+        _close(w.sum(-1), np.ones(w.shape[:3]), TOL, "weight rows sum to 1")
+        assert (w >= 0).all(), "negative weight"
+        if causal:
+            upper = np.triu(np.ones((24, 24), dtype=bool), 1)
+            assert (w[..., upper] == 0).all(), "masked weight not exactly 0"
+        _close(o, w @ v, TOL, "O = A V")
+
+
+def pin_values_ones(orc):
+    rng = _rng(4)
+    for causal in (False, True):
+        q = _randn(rng, 2, 4, 19, 16) * 3
+        k = _randn(rng, 2, 2, 19, 16) * 3
+        v = np.ones((2, 2, 19, 16))
+        o, _ = orc.attn(q, k, v, 0.25, causal)
+        _close(o, np.ones_like(o), 1e-14, "V = ones gives O = ones")
+
+
+def _prefix_mean(v, causal, Nq):
+    # mean of the visible value rows; square causal: rows 0..i
+    if causal:
+        cs = np.cumsum(v, axis=-2)
+        cnt = np.arange(1, v.shape[-2] + 1)[:, None]
+        return (cs / cnt)[..., :Nq, :]
+    return np.broadcast_to(v.mean(axis=-2, keepdims=True), v.shape[:-2] + (Nq, v.shape[-1]))
+
+
+def pin_identical_keys(orc):
+    rng = _rng(5)
+    N, d = 21, 8
+    for causal in (False, True):
+        q = _randn(rng, 1, 1, N, d)
+        kap = _randn(rng, d)
+        k = np.broadcast_to(kap, (1, 1, N, d)).copy()
+        v = _randn(rng, 1, 1, N, d)
+        scale = 0.4
+        o, lse = orc.attn(q, k, v, scale, causal)
+        _close(o, _prefix_mean(v, causal, N), 1e-13, "identical keys: O = mean of visible V")
+        nvis = np.arange(1, N + 1) if causal else np.full(N, N)
+        s = scale * (q[0, 0] @ kap)
+        _close(lse[0, 0], s + np.log(nvis), 1e-12, "identical keys: lse = s + ln n")
+
+
+def pin_zero_keys(orc):
+    rng = _rng(6)
+    N, d = 13, 4
+    for causal in (False, True):
+        q = _randn(rng, 1, 1, N, d)
+        k = np.zeros((1, 1, N, d))
+        v = _randn(rng, 1, 1, N, d)
+        o, lse = orc.attn(q, k, v, 1.0, causal)
+        nvis = np.arange(1, N + 1) if causal else np.full(N, N)
+        assert np.array_equal(lse[0, 0], np.log(nvis.astype(np.float64))), "K = 0: lse = ln n exactly"
+        _close(o, _prefix_mean(v, causal, N), 1e-14, "K = 0: O = mean of visible V")
+
+
+def pin_causal_row0(orc):
+    rng = _rng(7)
+    q = _randn(rng, 2, 3, 9, 8)
+    k = _randn(rng, 2, 3, 9, 8)
+    v = _randn(rng, 2, 3, 9, 8)
+    o, lse = orc.attn(q, k, v, 0.3, True)
+    assert np.array_equal(o[:, :, 0, :], v[:, :, 0, :]), "causal row 0 must return v_0 exactly"
+    _close(lse[:, :, 0], 0.3 * np.einsum("bhc,bhc->bh", q[:, :, 0], k[:, :, 0]), 1e-14,
+           "causal row 0: lse = s_00")
+
+
+def pin_shift_invariance(orc):
+    """K' = K + 1 w^T adds scale * q_i.w to every score of row i: O is
+    unchanged and lse shifts by that amount ([IO] sec. 8).  Shifts reach
+    +-1000, far beyond exp's fp64 range, so a softmax without the max
+    subtraction overflows."""
+    rng = _rng(8)
+    B, H, N, d = 1, 2, 16, 8
+    q = _randn(rng, B, H, N, d)
+    k = _randn(rng, B, H, N, d)
+    v = _randn(rng, B, H, N, d)
+    scale = 1.0 / np.sqrt(d)
+    for causal in (False, True):
+        o, lse = orc.attn(q, k, v, scale, causal)
+        for mag in (3.0, 1000.0):
+            w = _randn(rng, d)
+            w = w / np.linalg.norm(w)
+            # scale the shift so that max_i |scale * q_i . w| = mag
+            qs = scale * (q[0] @ w)
+            w = w * (mag / np.abs(qs).max())
+            k2 = k + w
+            o2, lse2 = orc.attn(q, k2, v, scale, causal)
+            shift = scale * (q @ w)
+            _close(o2, o, 1e-10 if mag < 100 else 1e-8, "shift invariance O (|c| <= %g)" % mag)
+            _close(lse2, lse + shift, 1e-9 * max(1.0, mag), "shift: lse + c (|c| <= %g)" % mag)
+
+
+def pin_permutation(orc):
+    """[E] sec. 5.1: without a mask, permuting the sequence permutes the
+    output; permuting K and V rows jointly changes nothing."""
+    rng = _rng(9)
+    q = _randn(rng, 1, 2, 11, 6)
+    k = _randn(rng, 1, 2, 15, 6)
+    v = _randn(rng, 1, 2, 15, 6)
+    o, lse = orc.attn(q, k, v, 0.5, False)
+    pk = rng.permutation(15)
+    o2, lse2 = orc.attn(q, k[:, :, pk], v[:, :, pk], 0.5, False)
+    _close(o2, o, 1e-13, "K/V permutation")
+    _close(lse2, lse, 1e-13, "K/V permutation lse")
+    pq = rng.permutation(11)
+    o3, lse3 = orc.attn(q[:, :, pq], k, v, 0.5, False)
+    _close(o3, o[:, :, pq], 0.0, "Q permutation")
+    _close(lse3, lse[:, :, pq], 0.0, "Q permutation lse")
+
+
+def pin_gqa_repeat(orc):
+    """[E] sec. 2.3, contiguous grouping: GQA equals MHA with each K/V head
+    repeated for the G query heads of its group."""
+    rng = _rng(10)
+    for (Hq, Hkv) in ((6, 3), (8, 2), (4, 1)):
+        G = Hq // Hkv
+        q = _randn(rng, 2, Hq, 10, 4)
+        k = _randn(rng, 2, Hkv, 12, 4)
+        v = _randn(rng, 2, Hkv, 12, 4)
+        for causal in (False, True):
+            o, lse = orc.attn(q, k, v, 0.5, causal)
+            o2, lse2 = orc.attn(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), 0.5, causal)
+            _close(o, o2, 0.0, "GQA == repeated MHA")
+            _close(lse, lse2, 0.0, "GQA == repeated MHA lse")
+
+
+def pin_chunked_prefill_alignment(orc):
+    """Causal with Nq < Nk: the Nq queries are the LAST Nq positions, so their
+    rows equal the last Nq rows of square causal attention over all Nk
+    positions ([R] sec. 4.1 defines the square case)."""
+    rng = _rng(11)
+    Nk, d = 23, 8
+    qf = _randn(rng, 1, 2, Nk, d)
+    k = _randn(rng, 1, 2, Nk, d)
+    v = _randn(rng, 1, 2, Nk, d)
+    of, lf = orc.attn(qf, k, v, 0.3, True)
+    for Nq in (1, 5, 22, 23):
+        o, lse = orc.attn(qf[:, :, Nk - Nq:], k, v, 0.3, True)
+        _close(o, of[:, :, Nk - Nq:], 0.0, "chunked prefill == last rows of full causal (Nq=%d)" % Nq)
+        _close(lse, lf[:, :, Nk - Nq:], 0.0, "chunked prefill lse")
+
+
+def pin_decode_is_last_row(orc):
+    """[N]: a decode query attends to every cached row; it equals the last row
+    of causal attention over the sequence so far."""
+    rng = _rng(12)
+    B, Hq, Hkv, Lmax, d = 3, 4, 2, 20, 8
+    kc = _randn(rng, B, Hkv, Lmax, d)
+    vc = _randn(rng, B, Hkv, Lmax, d)
+    q = _randn(rng, B, Hq, d)
+    sl = np.array([20, 7, 1], dtype=np.int32)
+    o, lse = orc.decode(q, kc, vc, sl, 0.35)
+    for b in range(B):
+        L = int(sl[b])
+        qf = _randn(rng, 1, Hq, L, d)
+        qf[0, :, L - 1] = q[b]
+        of, lf = orc.attn(qf, kc[b:b + 1, :, :L], vc[b:b + 1, :, :L], 0.35, True)
+        _close(o[b], of[0, :, L - 1], 0.0, "decode == last causal row (b=%d)" % b)
+        _close(lse[b], lf[0, :, L - 1], 0.0, "decode lse == last causal row")
+    # padding rows are never read: poison them
+    kp, vp = kc.copy(), vc.copy()
+    for b in range(B):
+        kp[b, :, sl[b]:] = np.nan
+        vp[b, :, sl[b]:] = np.nan
+    o2, lse2 = orc.decode(q, kp, vp, sl, 0.35)
+    _close(o2, o, 0.0, "decode ignores rows beyond seq_len")
+    # empty and over-long sequences
+    o3, lse3 = orc.decode(q, kc, vc, np.array([0, 99, -5], dtype=np.int32), 0.35)
+    assert (o3[0] == 0).all() and np.isneginf(lse3[0]).all(), "seq_len 0: O = 0, lse = -inf"
+    assert (o3[2] == 0).all() and np.isneginf(lse3[2]).all(), "negative seq_len clamps to 0"
+    o4, lse4 = orc.decode(q[1:2], kc[1:2], vc[1:2], np.array([Lmax], dtype=np.int32), 0.35)
+    _close(o3[1], o4[0], 0.0, "seq_len above Lmax clamps to Lmax")
+
+
+def pin_blockwise_equals_direct(orc):
+    """[R] sec. 6.3 / [IO] eqs. (1)-(2): the blockwise recurrence reaches the
+    direct result, for any block size, dividing or not."""
+    rng = _rng(13)
+    N = 37
+    q = _randn(rng, 1, 2, N, 8) * 2
+    k = _randn(rng, 1, 2, N, 8) * 2
+    v = _randn(rng, 1, 2, N, 8)
+    for causal in (False, True):
+        o, lse = orc.attn(q, k, v, 0.5, causal)
+        for beta in (1, 3, 16, 64, N):
+            ob, lb = orc.blockwise(q, k, v, 0.5, causal, beta)
+            _close(ob, o, TOL, "blockwise beta=%d causal=%s" % (beta, causal))
+            _close(lb, lse, TOL, "blockwise lse beta=%d" % beta)
+
+
+def pin_rows_entry_matches_full(orc):
+    rng = _rng(14)
+    q = _randn(rng, 2, 4, 30, 8)
+    k = _randn(rng, 2, 2, 30, 8)
+    v = _randn(rng, 2, 2, 30, 8)
+    for causal in (False, True):
+        o, lse = orc.attn(q, k, v, 0.3, causal)
+        rows = np.array([[0, 0, 0], [1, 3, 29], [0, 2, 17], [1, 1, 5]], dtype=np.int32)
+        orr, lr = orc.attn_rows(q, k, v, 0.3, causal, rows)
+        _close(orr, o[rows[:, 0], rows[:, 1], rows[:, 2]], 0.0, "attn_rows == attn")
+        _close(lr, lse[rows[:, 0], rows[:, 1], rows[:, 2]], 0.0, "attn_rows lse")
+
+
+ALL_PINS = [
+    pin_decimal_bruteforce,
+    pin_torch_sdpa,
+    pin_rows_sum_to_one,
+    pin_values_ones,
+    pin_identical_keys,
+    pin_zero_keys,
+    pin_causal_row0,
+    pin_shift_invariance,
+    pin_permutation,
+    pin_gqa_repeat,
+    pin_chunked_prefill_alignment,
+    pin_decode_is_last_row,
+    pin_blockwise_equals_direct,
+    pin_rows_entry_matches_full,
+]
