@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one pass of the whole path over synthetic inputs already resident
+in device memory:
+  * prefill: attn_fwd on the GQA workload (B=1, 64 query heads over 8 KV heads,
+    N=8192, d=128, bf16, causal), and
+  * decode:  attn_decode on the KV-cache workload (16 sequences, 32 query heads
+    over 8 KV heads, d=128, bf16 cache, lengths uniform in [512, 4096]); each
+    step reads one of 4 distinct cache replicas (>= 600 MB together), so the
+    cache is read from HBM rather than from the 256 MB last-level cache.
+
+The JSON line reports the prefill throughput in TFLOP/s as `value` (algorithmic
+FLOPs: 4*d per visible query/key pair), the decode bandwidth in GB/s (valid
+cache rows plus q, o, lse) in `decode`, and for each kernel its roofline
+fraction from its average duration measured with HIP events on the stream the
+kernels run on.  `cpu_baseline` times the fp64 oracle on a bounded sample of the
+prefill rows on the host cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak (prefill); KV-cache GB/s & % HBM (decode)"
+N_REPLICAS = 4
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target seconds of oracle work")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="run one kernel only (for profiling runs)")
+    return ap.parse_args()
+
+
+def stored_traffic(kernel):
+    """Per-launch HBM bytes from the committed counter summary, or None when
+    it is absent or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    from exact_scaled_dot_sdpa_amd.build import source_digest
+
+    if t.get("kernel_source_digest") != source_digest():
+        return None
+    e = t.get("kernels", {}).get(kernel)
+    return None if e is None else e.get("bytes_per_launch")
+
+
+def cpu_baseline(q, k, v, w, target_s):
+    """The oracle, as it stands, on a bounded sample of prefill rows."""
+    import numpy as np
+
+    import oracle
+    from exact_scaled_dot_sdpa_amd import inputs as I
+
+    nthreads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    qd, kd, vd = I.to_f64(q), I.to_f64(k), I.to_f64(v)
+    rng = np.random.default_rng(12345)
+
+    def sample(n):
+        b = np.zeros(n, dtype=np.int32)
+        h = rng.integers(0, w.Hq, n).astype(np.int32)
+        i = rng.integers(0, w.N, n).astype(np.int32)
+        return np.stack([b, h, i], axis=1)
+
+    def flops(rows):
+        # 4*d per visible pair; row i of a causal square head sees i+1 keys
+        return float(4 * w.d * (rows[:, 2].astype(np.int64) + 1).sum())
+
+    rows = sample(max(64, nthreads * 4))
+    t0 = time.perf_counter()
+    oracle.attn_rows(qd, kd, vd, w.scale, w.causal, rows, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    rate = flops(rows) / max(dt, 1e-6)
+    n = int(min(max(64, rows.shape[0] * max(target_s, 0.5) / max(dt, 1e-6)), w.Hq * w.N))
+    rows = sample(n)
+    t0 = time.perf_counter()
+    oracle.attn_rows(qd, kd, vd, w.scale, w.causal, rows, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    f = flops(rows)
+    return {
+        "value": f / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": nthreads,
+        "kind": "oracle",
+        "sample": "%d random (head, row) pairs of the GQA causal prefill workload (%.3g GFLOP of the "
+                  "%.4g GFLOP total), fp64, %.1f s; calibration rate %.3g GFLOP/s"
+                  % (n, f / 1e9, 4.0 * w.d * w.Hq * w.N * (w.N + 1) / 2 / 1e9, dt, rate / 1e9),
+        "seconds": dt,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(asked for --gpus %d)." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_scaled_dot_sdpa_amd as E
+    from exact_scaled_dot_sdpa_amd import accounting as A
+    from exact_scaled_dot_sdpa_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    wp = I.WORKLOADS["C4"]
+    wd = I.WORKLOADS["C5"]
+    run_p = args.only in (None, "prefill")
+    run_d = args.only in (None, "decode")
+
+    # ---- inputs, resident in HBM before timing --------------------------
+    q_cpu, k_cpu, v_cpu = I.workload_inputs("C4")
+    q, k, v = q_cpu.to(dev), k_cpu.to(dev), v_cpu.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    sl_cpu, qd_cpu, kc_cpu, vc_cpu = I.workload_inputs("C5")
+    qd, sl = qd_cpu.to(dev), sl_cpu.to(dev)
+    caches = [(kc_cpu.to(dev), vc_cpu.to(dev)) for _ in range(N_REPLICAS)]
+    od = torch.empty_like(qd)
+    lsed = torch.empty(qd.shape[:2], dtype=torch.float32, device=dev)
+    ws = torch.empty(E.attn_decode_workspace_bytes(wd.B, wd.Hq, wd.Hkv, wd.Lmax, wd.d), dtype=torch.uint8,
+                     device=dev)
+
+    p_flops = A.prefill_flops(wp.B, wp.Hq, wp.N, wp.N, wp.d, wp.causal)
+    p_bytes = A.prefill_bytes(wp.B, wp.Hq, wp.Hkv, wp.N, wp.N, wp.d, wp.dtype)
+    d_bytes = A.decode_bytes(sl_cpu.tolist(), wd.Hq, wd.Hkv, wd.d, wd.dtype)
+    d_flops = A.decode_flops(sl_cpu.tolist(), wd.Hq, wd.d)
+
+    def prefill():
+        E.attn_fwd(q, k, v, scale=wp.scale, causal=wp.causal, o=o, lse=lse)
+
+    def decode(r):
+        kc, vc = caches[r % N_REPLICAS]
+        E.attn_decode(qd, kc, vc, sl, scale=wd.scale, o=od, lse=lsed, workspace=ws)
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for i in range(args.warmup):
+        if run_p:
+            prefill()
+        if run_d:
+            decode(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        if run_p:
+            prefill()
+        ev[i][1].record(stream)
+        if run_d:
+            decode(i)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    p_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    d_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    ms_per_step = wall * 1e3 / K
+
+    p_tflops = p_flops / (p_ms * 1e-3) / 1e12 if run_p else None
+    d_gbs = d_bytes / (d_ms * 1e-3) / 1e9 if run_d else None
+
+    out = {
+        "metric": METRIC,
+        "value": round(p_tflops, 2) if run_p else None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: iid N(0,1) from seeded CPU generators, rounded to bf16",
+        "config": {
+            "workload": "GQA causal prefill B=1 Hq=64 Hkv=8 N=8192 d=128 bf16 + KV-cache decode B=16 "
+                        "Hq=32 Hkv=8 d=128 bf16 L~U[512,4096]",
+            "prefill": {"B": wp.B, "Hq": wp.Hq, "Hkv": wp.Hkv, "N": wp.N, "d": wp.d, "causal": wp.causal,
+                        "flops_per_launch": p_flops, "bytes_per_launch": p_bytes},
+            "decode": {"B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "Lmax": wd.Lmax, "d": wd.d,
+                       "sum_seq_len": int(sl_cpu.sum()), "bytes_per_launch": d_bytes,
+                       "flops_per_launch": d_flops, "cache_replicas": N_REPLICAS},
+            "parallelism": "single GPU",
+        },
+    }
+    if run_p:
+        tr = stored_traffic("prefill")
+        out["roofline"] = {
+            "bound": "mfma", "achieved": round(p_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4), "traffic": tr,
+            "kernel": "prefill_bf16_kernel<128,true>", "avg_launch_ms": round(p_ms, 5),
+        }
+    if run_d:
+        tr = stored_traffic("decode")
+        out["decode"] = {"value": round(d_gbs, 1), "unit": "GB/s", "frac_hbm": round(d_gbs / PEAK_HBM_GBS, 4),
+                         "avg_launch_ms": round(d_ms, 5),
+                         "tflops": round(d_flops / (d_ms * 1e-3) / 1e12, 2)}
+        out["roofline_decode"] = {
+            "bound": "hbm", "achieved": round(d_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(d_gbs / PEAK_HBM_GBS, 4), "traffic": tr,
+            "kernel": "decode_split_kernel<128,4> + decode_merge_kernel<128>", "avg_launch_ms": round(d_ms, 5),
+        }
+    if not args.no_cpu_baseline and run_p:
+        out["cpu_baseline"] = cpu_baseline(q_cpu, k_cpu, v_cpu, wp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

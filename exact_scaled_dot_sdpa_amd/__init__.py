@@ -1,0 +1,42 @@
+"""Exact scaled dot-product attention on MI355X (gfx950).
+
+A thin binding over libattn.so (the C ABI in include/attn.h).  Every step of the
+computation runs in the library's HIP kernels; this module only checks tensor
+metadata and passes device pointers, sizes and the current HIP stream.  PyTorch
+provides device memory and streams.
+
+Functions carry the names of the C entry points:
+
+    attn_fwd(q, k, v, scale=None, causal=False, o=None, lse=None, return_lse=True)
+    attn_decode(q, k_cache, v_cache, seq_lens, scale=None, o=None, lse=None,
+                workspace=None, keys_per_split=0, return_lse=True)
+    attn_decode_workspace_bytes(B, Hq, Hkv, max_seq_len, d, keys_per_split=0)
+    attn_status_str(status)
+
+There is no fallback: if libattn.so is missing or a call fails, an exception is
+raised.
+"""
+from ._binding import (  # noqa: F401
+    ATTN_BF16,
+    ATTN_ERR_INVALID_ARG,
+    ATTN_ERR_LAUNCH,
+    ATTN_ERR_UNSUPPORTED,
+    ATTN_ERR_WORKSPACE,
+    ATTN_F32,
+    ATTN_OK,
+    AttnError,
+    attn_decode,
+    attn_decode_workspace_bytes,
+    attn_fwd,
+    attn_status_str,
+    lib,
+    lib_path,
+)
+
+__all__ = [
+    "attn_fwd",
+    "attn_decode",
+    "attn_decode_workspace_bytes",
+    "attn_status_str",
+    "AttnError",
+]

@@ -1,0 +1,148 @@
+"""Summaries of rocprofv3 output for the profiles/ folder.
+
+    python -m exact_scaled_dot_sdpa_amd.profiling stats KERNEL_STATS_CSV --cmd "..." --out FILE.md
+    python -m exact_scaled_dot_sdpa_amd.profiling traffic --fetch FETCH_CSV --write WRITE_CSV \
+        --calib-mib 512 --cmd-fetch "..." --cmd-write "..." --json profiles/traffic.json --out FILE.md
+
+`stats` condenses a `rocprofv3 --kernel-trace --stats -f csv` kernel_stats file
+into a short table.  `traffic` turns two `rocprofv3 --pmc FETCH_SIZE` /
+`--pmc WRITE_SIZE` counter files (KiB per dispatch) into HBM bytes per launch:
+each counter is scaled by the factor that makes the plain device copy of
+--calib-mib MiB (launched by `bench.py --calib-copy-mib`) read and write
+exactly that many bytes.  The JSON records the kernel-source digest; bench.py
+reports the bytes only while the kernels are unchanged.
+"""
+import argparse
+import csv
+import json
+import os
+import statistics
+import sys
+
+KERNELS = {
+    # logical kernel -> substrings of the dispatched kernel names that make one launch
+    "prefill": ["prefill_bf16_kernel"],
+    "decode": ["decode_split_kernel", "decode_merge_kernel"],
+}
+COPY_KERNEL = "copyBuffer"
+
+
+def _short(name):
+    for key in ("prefill_bf16_kernel", "prefill_f32_kernel", "decode_split_kernel", "decode_merge_kernel"):
+        if key in name:
+            return key
+    return name[:60]
+
+
+def stats(path, cmd, out):
+    rows = list(csv.DictReader(open(path)))
+    lines = ["# rocprofv3 kernel statistics", "", "Command:", "", "```", cmd, "```", "",
+             "| kernel | calls | avg (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append("| %s | %s | %.2f | %.2f | %.2f | %.2f%% |" % (
+            _short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    lines += ["", "Full kernel names:", ""] + ["- `%s`" % r["Name"] for r in rows]
+    text = "\n".join(lines) + "\n"
+    with open(out, "w") as f:
+        f.write(text)
+    return text
+
+
+def _per_dispatch(path, counter):
+    res = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        res.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return res
+
+
+def _calib(values, calib_kib):
+    # the copy of calib_kib KiB is the largest copyBuffer dispatch
+    cands = [v for name, vs in values.items() if COPY_KERNEL in name for v in vs]
+    if not cands:
+        raise SystemExit("no %s dispatch found for calibration" % COPY_KERNEL)
+    return calib_kib / max(cands), max(cands)
+
+
+def traffic(fetch_csv, write_csv, calib_mib, cmd_fetch, cmd_write, json_out, out):
+    from exact_scaled_dot_sdpa_amd.build import source_digest
+
+    calib_kib = calib_mib * 1024.0
+    fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _per_dispatch(write_csv, "WRITE_SIZE")
+    f_fac, f_raw = _calib(fetch, calib_kib)
+    w_fac, w_raw = _calib(write, calib_kib)
+    kernels = {}
+    for logical, parts in KERNELS.items():
+        fk = wk = 0.0
+        found = True
+        detail = {}
+        for part in parts:
+            fv = [v for n, vs in fetch.items() if part in n for v in vs]
+            wv = [v for n, vs in write.items() if part in n for v in vs]
+            if not fv or not wv:
+                found = False
+                break
+            detail[part] = {"fetch_kib_raw": statistics.median(fv), "write_kib_raw": statistics.median(wv),
+                            "dispatches": len(fv)}
+            fk += statistics.median(fv)
+            wk += statistics.median(wv)
+        if not found:
+            continue
+        read_b = fk * f_fac * 1024.0
+        write_b = wk * w_fac * 1024.0
+        kernels[logical] = {"bytes_per_launch": int(round(read_b + write_b)), "read_bytes": int(round(read_b)),
+                            "write_bytes": int(round(write_b)), "parts": detail}
+    doc = {
+        "kernel_source_digest": source_digest(),
+        "calibration": {"copy_mib": calib_mib, "fetch_kib_raw": f_raw, "write_kib_raw": w_raw,
+                        "fetch_factor": f_fac, "write_factor": w_fac},
+        "commands": {"fetch": cmd_fetch, "write": cmd_write},
+        "kernels": kernels,
+    }
+    with open(json_out, "w") as f:
+        json.dump(doc, f, indent=1)
+        f.write("\n")
+    lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+             "Commands:", "", "```", cmd_fetch, cmd_write, "```", "",
+             "Calibration: one plain device copy of %d MiB reads %.1f KiB by FETCH_SIZE and writes %.1f KiB by "
+             "WRITE_SIZE, so FETCH_SIZE is scaled by %.4f and WRITE_SIZE by %.4f." % (
+                 calib_mib, f_raw, w_raw, f_fac, w_fac), "",
+             "Kernel-source digest: `%s`" % doc["kernel_source_digest"], "",
+             "| kernel | read (MB) | write (MB) | total (MB) |", "|---|---|---|---|"]
+    for k, e in kernels.items():
+        lines.append("| %s | %.2f | %.2f | %.2f |" % (k, e["read_bytes"] / 1e6, e["write_bytes"] / 1e6,
+                                                      e["bytes_per_launch"] / 1e6))
+    text = "\n".join(lines) + "\n"
+    with open(out, "w") as f:
+        f.write(text)
+    return text
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--calib-mib", type=int, required=True)
+    t.add_argument("--cmd-fetch", required=True)
+    t.add_argument("--cmd-write", required=True)
+    t.add_argument("--json", required=True)
+    t.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    if a.what == "stats":
+        print(stats(a.csv, a.cmd, a.out))
+    else:
+        print(traffic(a.fetch, a.write, a.calib_mib, a.cmd_fetch, a.cmd_write, a.json, a.out))
+
+
+if __name__ == "__main__":
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    main()

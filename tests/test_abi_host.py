@@ -1,0 +1,114 @@
+"""Host-side checks of libattn.so (CPU only): the library loads, exports every
+entry point include/attn.h declares, and rejects invalid arguments before any
+HIP runtime call.  No call made here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_scaled_dot_sdpa_amd as E
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+P = 1 << 20  # a 16-byte aligned fake device address; never dereferenced here
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char|void)\s*\*?\s*(attn_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert names == sorted(["attn_fwd", "attn_decode", "attn_decode_workspace_bytes", "attn_status_str"])
+    lib = ctypes.CDLL(E.lib_path())
+    for n in names:
+        assert hasattr(lib, n), "libattn.so does not export %s" % n
+
+
+def test_status_strings():
+    assert E.attn_status_str(0) == "ATTN_OK"
+    assert E.attn_status_str(1) == "ATTN_ERR_INVALID_ARG"
+    assert E.attn_status_str(2) == "ATTN_ERR_UNSUPPORTED"
+    assert E.attn_status_str(3) == "ATTN_ERR_WORKSPACE"
+    assert E.attn_status_str(4) == "ATTN_ERR_LAUNCH"
+    assert E.attn_status_str(99) == "ATTN_ERR_UNKNOWN"
+
+
+def fwd(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64, scale=0.125, causal=0, dtype=1):
+    return E.lib().attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=3, Hkv=2), E.ATTN_ERR_INVALID_ARG),        # Hq % Hkv != 0
+    (dict(Hq=0), E.ATTN_ERR_INVALID_ARG),
+    (dict(Hkv=0), E.ATTN_ERR_INVALID_ARG),
+    (dict(B=-1), E.ATTN_ERR_INVALID_ARG),
+    (dict(Nq=-1), E.ATTN_ERR_INVALID_ARG),
+    (dict(Nk=-1), E.ATTN_ERR_INVALID_ARG),
+    (dict(d=96), E.ATTN_ERR_UNSUPPORTED),
+    (dict(d=256), E.ATTN_ERR_UNSUPPORTED),
+    (dict(causal=1, Nq=9, Nk=8), E.ATTN_ERR_INVALID_ARG),  # causal needs Nq <= Nk
+    (dict(scale=float("nan")), E.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), E.ATTN_ERR_INVALID_ARG),
+    (dict(dtype=7), E.ATTN_ERR_INVALID_ARG),
+    (dict(q=None), E.ATTN_ERR_INVALID_ARG),
+    (dict(o=None), E.ATTN_ERR_INVALID_ARG),
+    (dict(k=None), E.ATTN_ERR_INVALID_ARG),
+    (dict(q=P + 2), E.ATTN_ERR_INVALID_ARG),            # misaligned
+    (dict(v=P + 8), E.ATTN_ERR_INVALID_ARG),
+    (dict(lse=P + 2), E.ATTN_ERR_INVALID_ARG),
+    (dict(B=0), E.ATTN_OK),                              # empty: no-op
+    (dict(Nq=0), E.ATTN_OK),
+    (dict(Nq=0, Nk=0, causal=1), E.ATTN_OK),
+])
+def test_fwd_validation(kw, status):
+    assert fwd(**kw) == status
+
+
+def dec(q=P, kc=P, vc=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Lmax=512, d=128, scale=0.09, kps=0, dtype=1,
+        ws=P, ws_bytes=1 << 30):
+    return E.lib().attn_decode(q, kc, vc, sl, o, lse, B, Hq, Hkv, Lmax, d, scale, kps, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=6, Hkv=4), E.ATTN_ERR_INVALID_ARG),
+    (dict(B=-1), E.ATTN_ERR_INVALID_ARG),
+    (dict(Lmax=-1), E.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), E.ATTN_ERR_INVALID_ARG),
+    (dict(kps=100), E.ATTN_ERR_INVALID_ARG),            # not a multiple of 64
+    (dict(kps=32), E.ATTN_ERR_INVALID_ARG),
+    (dict(kps=1 << 17), E.ATTN_ERR_INVALID_ARG),
+    (dict(dtype=0), E.ATTN_ERR_UNSUPPORTED),            # fp32 decode not implemented
+    (dict(d=96), E.ATTN_ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=2), E.ATTN_ERR_UNSUPPORTED),        # group of 3
+    (dict(Hq=64, Hkv=2), E.ATTN_ERR_UNSUPPORTED),       # group of 32
+    (dict(sl=None), E.ATTN_ERR_INVALID_ARG),
+    (dict(sl=P + 2), E.ATTN_ERR_INVALID_ARG),
+    (dict(q=None), E.ATTN_ERR_INVALID_ARG),
+    (dict(kc=P + 4), E.ATTN_ERR_INVALID_ARG),
+    (dict(ws=None), E.ATTN_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), E.ATTN_ERR_WORKSPACE),
+    (dict(ws=P + 4), E.ATTN_ERR_WORKSPACE),
+    (dict(B=0), E.ATTN_OK),
+])
+def test_decode_validation(kw, status):
+    assert dec(**kw) == status
+
+
+def test_decode_workspace_bytes():
+    f = E.attn_decode_workspace_bytes
+    # default split of 256 keys: S = ceil(4096 / 256) = 16
+    rows = 16 * 32 * 16
+    assert f(16, 32, 8, 4096, 128) == ((rows * 128 * 4 + 255) // 256) * 256 + rows * 4
+    assert f(16, 32, 8, 4096, 128, 1024) == 16 * 32 * 4 * 128 * 4 + 16 * 32 * 4 * 4
+    assert f(1, 1, 1, 0, 64) == 256 + 4            # at least one split
+    assert f(1, 3, 2, 100, 64) == 0                  # invalid sizes
+    assert f(1, 2, 1, 100, 96) == 0
+    assert f(1, 2, 1, 100, 64, 100) == 0
+    # exactly the workspace that size reports is accepted, one byte less is not
+    need = f(2, 8, 2, 512, 128)
+    assert dec(ws_bytes=need - 1) == E.ATTN_ERR_WORKSPACE

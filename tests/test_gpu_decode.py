@@ -1,0 +1,105 @@
+"""Parity of attn_decode (the split-KV HIP kernels) with the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import exact_scaled_dot_sdpa_amd as E
+from exact_scaled_dot_sdpa_amd import inputs as I
+from gpu_util import TOL_LSE, TOL_O, assert_close, dev, gpu_decode, gpu_fwd, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _parity(orc, seq_lens, q, kc, vc, scale, label, kps=0):
+    say("[decode] %s q%s cache%s kps=%d L=%s" % (label, tuple(q.shape), tuple(kc.shape), kps,
+                                                 seq_lens.tolist()[:8]))
+    o, lse = gpu_decode(seq_lens, q, kc, vc, scale, kps)
+    o_ref, lse_ref = orc.decode(I.to_f64(q), I.to_f64(kc), I.to_f64(vc), seq_lens.numpy(), scale)
+    assert_close(label + " O", o, o_ref, TOL_O["bf16"])
+    assert_close(label + " LSE", lse, lse_ref, TOL_LSE)
+    return o, lse
+
+
+def test_c5_full_parity(orc):
+    """The KV-cache decode workload at full size (default split)."""
+    w = I.WORKLOADS["C5"]
+    sl, q, kc, vc = I.workload_inputs("C5")
+    _parity(orc, sl, q, kc, vc, w.scale, "C5")
+
+
+@pytest.mark.parametrize("kps", [64, 128, 512, 4096])
+def test_split_count_invariance(orc, kps):
+    sl, q, kc, vc = I.decode_inputs(4, 32, 8, 2048, 128, "bf16", seed=61, lo=1, hi=2048)
+    o_ref, l_ref = gpu_decode(sl, q, kc, vc, 0.088, 0)
+    o, l = _parity(orc, sl, q, kc, vc, 0.088, "split", kps)
+    assert_close("kps=%d vs default (LSE)" % kps, l, l_ref, 1e-5)
+    assert_close("kps=%d vs default (O)" % kps, o, o_ref, 2 ** -6)
+
+
+@pytest.mark.parametrize("G,d", [(1, 128), (2, 64), (4, 64), (8, 128), (16, 128), (16, 64)])
+def test_group_sizes(orc, G, d):
+    Hkv = 2
+    sl, q, kc, vc = I.decode_inputs(3, G * Hkv, Hkv, 700, d, "bf16", seed=70 + G, lo=1, hi=700)
+    _parity(orc, sl, q, kc, vc, 1.0 / np.sqrt(d), "G=%d d=%d" % (G, d))
+
+
+def test_edge_lengths(orc):
+    """seq_len 0 (O = 0, LSE = -inf), 1, a ragged tail, exactly one split, and
+    values beyond max_seq_len (clamped)."""
+    B, Hq, Hkv, Lmax, d = 6, 8, 2, 600, 128
+    _, q, kc, vc = I.decode_inputs(B, Hq, Hkv, Lmax, d, "bf16", seed=80)
+    sl = torch.tensor([0, 1, 257, 256, 600, 5000], dtype=torch.int32)
+    o, lse = gpu_decode(sl, q, kc, vc, 0.088)
+    assert (o[0] == 0).all() and np.isneginf(lse[0]).all()
+    o_ref, l_ref = orc.decode(I.to_f64(q), I.to_f64(kc), I.to_f64(vc), sl.numpy(), 0.088)
+    assert_close("edge lengths O", o, o_ref, TOL_O["bf16"])
+    assert_close("edge lengths LSE", lse, l_ref, TOL_LSE)
+
+
+def test_nan_padding_never_read():
+    """Cache rows at or beyond seq_len are poisoned with NaN; the result must
+    equal the unpoisoned one bit for bit."""
+    sl, q, kc, vc = I.decode_inputs(5, 16, 4, 1000, 128, "bf16", seed=90, lo=1, hi=999)
+    o1, l1 = gpu_decode(sl, q, kc, vc, 0.088)
+    kp, vp = kc.clone(), vc.clone()
+    for b, L in enumerate(sl.tolist()):
+        kp[b, :, L:] = float("nan")
+        vp[b, :, L:] = float("nan")
+    o2, l2 = gpu_decode(sl, q, kp, vp, 0.088)
+    assert np.isfinite(o2).all()
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_decode_matches_prefill_last_row(orc):
+    """A decode step equals the last row of causal prefill over the same rows."""
+    L, Hq, Hkv, d = 777, 8, 2, 128
+    g = torch.Generator().manual_seed(99)
+    qf = torch.randn(1, Hq, L, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(1, Hkv, L, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(1, Hkv, L, d, generator=g).to(torch.bfloat16)
+    op, lp = gpu_fwd(qf, k, v, 0.088, True)
+    od, ld = gpu_decode(torch.tensor([L], dtype=torch.int32), qf[:, :, L - 1].contiguous(), k, v, 0.088)
+    assert_close("decode vs prefill last row (LSE)", ld[0], lp[0, :, L - 1], 1e-5)
+    assert_close("decode vs prefill last row (O)", od[0], op[0, :, L - 1], 2 * TOL_O["bf16"])
+    o_ref, l_ref = orc.attn_rows(I.to_f64(qf), I.to_f64(k), I.to_f64(v), 0.088, True,
+                                 np.array([[0, h, L - 1] for h in range(Hq)], dtype=np.int32))
+    assert_close("decode vs oracle last row", od[0], o_ref, TOL_O["bf16"])
+
+
+def test_run_twice_bitwise():
+    sl, q, kc, vc = I.decode_inputs(8, 32, 8, 1024, 128, "bf16", seed=95, lo=1, hi=1024)
+    a = gpu_decode(sl, q, kc, vc, 0.088)
+    b = gpu_decode(sl, q, kc, vc, 0.088)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_workspace_reuse_and_explicit_buffer(orc):
+    sl, q, kc, vc = I.decode_inputs(4, 32, 8, 512, 128, "bf16", seed=97, lo=100, hi=512)
+    need = E.attn_decode_workspace_bytes(4, 32, 8, 512, 128)
+    ws = torch.full((need,), 0x7f, dtype=torch.uint8, device="cuda")  # garbage contents
+    o, lse = E.attn_decode(dev(q), dev(kc), dev(vc), dev(sl), workspace=ws)
+    torch.cuda.synchronize()
+    o_ref, l_ref = orc.decode(I.to_f64(q), I.to_f64(kc), I.to_f64(vc), sl.numpy(), 1 / np.sqrt(128))
+    assert_close("explicit workspace O", I.to_f64(o), o_ref, TOL_O["bf16"])
+    with pytest.raises(E.AttnError):
+        E.attn_decode(dev(q), dev(kc), dev(vc), dev(sl), workspace=ws[: need - 16])
