@@ -9,23 +9,31 @@
 // gfx950 mapping
 //   * A workgroup owns BM = 128 query rows of one (batch, query head); each of
 //     its 4 waves owns 32 rows.  K/V are streamed in tiles of BN = 64 keys.
+//   * K and V tiles go from HBM straight into LDS with global_load_lds_dwordx4
+//     (no staging registers, no VALU work), double-buffered so the next tile
+//     lands while the current one is computed; one barrier per tile.  Both
+//     tiles stay row-major in LDS with the 16-byte chunks of each row XOR-
+//     swizzled by a function of the row, which keeps the LDS reads below free
+//     of bank conflicts.
 //   * Scores are computed transposed, S^T = K Q^T, with
-//     v_mfma_f32_32x32x16_bf16: K (from LDS) is the A operand, Q^T (held in
-//     registers for the whole kernel) the B operand.  In the fp32 result every
-//     lane holds ONE query row (lane % 32) and 16 keys per 32-key block, the
-//     other 16 keys sitting in lane ^ 32.  Row max and row sum are therefore
-//     in-lane reductions plus a single exchange with lane ^ 32.
-//   * P^T, converted to bf16 in registers, is directly the B operand of
-//     O^T = V^T P^T (again 32x32x16), whose A operand V^T is read from LDS
-//     where the V tile is stored transposed with the keys of each 16-key
-//     group permuted (bits 2 and 3 of the key index swapped), so that each
-//     lane's 8 keys are one contiguous 16-byte LDS read.  No LDS round trip
-//     for P, no cross-lane shuffles for the rescale of O^T (one query per
-//     lane).
-//   * Softmax in base 2: t = s * (scale * log2 e); exp2 is v_exp_f32.
+//     v_mfma_f32_32x32x16_bf16: K (ds_read_b128 from LDS) is the A operand,
+//     Q^T (held in registers for the whole kernel) the B operand.  In the fp32
+//     result every lane holds ONE query row (lane % 32) and 16 keys per 32-key
+//     block, the other 16 keys sitting in lane ^ 32: row max and row sum are
+//     in-lane reductions plus (rarely) one exchange with lane ^ 32.
+//   * P^T, converted to bf16 in registers (v_cvt_pk_bf16_f32), is directly the
+//     B operand of O^T = V^T P^T (again 32x32x16).  Its A operand, V^T, is read
+//     from the row-major V tile with ds_read_b64_tr_b16: a 16-lane group reads
+//     a 4-key x 16-column block and each lane receives 4 keys of one column,
+//     exactly the operand layout.  No transposed copy is ever stored.
+//   * Softmax in base 2: p = exp2(s * scale * log2 e - m), one FMA + v_exp_f32.
+//     The subtracted reference m is raised (and O^T, l rescaled) only when a
+//     row's max outgrows it by more than 2^8, which leaves u / l unchanged
+//     ("从注意力到 IO 感知执行", sec. 8: the subtracted value only changes the
+//     representation) and removes the per-tile rescale.
 //   * Causal: tiles beyond the last visible key of the workgroup are never
-//     loaded; only tiles that straddle the diagonal (or the end of K) apply
-//     the element mask.  Bottom-right alignment: row i sees j <= i + Nk - Nq.
+//     loaded; only tiles that straddle the diagonal (or the end of K) take the
+//     masked code path.  Bottom-right alignment: row i sees j <= i + Nk - Nq.
 //   * GQA: query head h reads K/V head h / (Hq / Hkv).  Work items are
 //     ordered (batch, KV head) outermost, then query tile (heaviest causal
 //     tile first), then the G query heads of the group, and spread over the
@@ -44,31 +52,41 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int BM = 128;  // query rows per workgroup
 constexpr int BN = 64;   // keys per tile
 constexpr int NTHR = 256;
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float LOG2E = 1.44269504088896340736f;
+constexpr float RESCALE_TH = 8.f;  // reference lag allowed before O is rescaled (base-2 units)
 
 template <int D>
 struct Cfg {
-    static constexpr int KST = D + 8;    // LDS row stride of K, elements (16 B pad)
-    static constexpr int VST = BN + 8;   // LDS row stride of V^T, elements (16 B pad)
-    static constexpr int KS = D / 16;    // k-steps of the score MFMA
-    static constexpr int CB = D / 32;    // 32-column blocks of O^T
-    static constexpr int CH = D / 8;     // 16-byte chunks per row
-    static constexpr int KLD = BN * CH / NTHR;  // 16-byte K loads per thread
-    static constexpr int KPT = D / 32;   // keys per thread when staging V
-    static constexpr int VA = BN / KPT;  // key groups per tile when staging V
-    static_assert(KLD * NTHR == BN * CH, "K tile split");
-    static_assert(VA * CH == NTHR, "V tile split");
+    static constexpr int CH = D / 8;               // 16-byte chunks per row
+    static constexpr int KS = D / 16;              // k-steps of the score MFMA
+    static constexpr int CB = D / 32;              // 32-column blocks of O^T
+    static constexpr int RPW = 64 / CH;            // rows one wave-wide 16-byte load covers
+    static constexpr int ROUNDS = BN / (4 * RPW);  // such loads per wave per tile
+    static constexpr int TILE = BN * D;            // elements of one K or V tile
+    static_assert(ROUNDS * 4 * RPW == BN, "tile split");
 };
 
-// Position of key j (0..BN-1) inside a transposed V row: bits 2 and 3 swapped.
-__device__ __forceinline__ int vperm(int j) {
-    return (j & ~12) | ((j >> 1) & 4) | ((j << 1) & 8);
-}
+// XOR swizzles of the 16-byte chunk index within a row.
+//   K rows are read 16 rows x one chunk at a time (ds_read_b128): 16
+//   consecutive rows must land on 16 different 16-byte bank slots.
+//   V rows are read 4 rows x 4 adjacent chunks at a time (transposing
+//   loads of two 16-lane groups): 4 consecutive rows must land on disjoint
+//   groups of 4 bank slots.
+template <int D> __device__ __forceinline__ int swz_k(int row);
+template <> __device__ __forceinline__ int swz_k<128>(int row) { return row & 15; }
+template <> __device__ __forceinline__ int swz_k<64>(int row) { return (row >> 1) & 7; }
+template <int D> __device__ __forceinline__ int swz_v(int row);
+template <> __device__ __forceinline__ int swz_v<128>(int row) { return (row & 3) << 2; }
+template <> __device__ __forceinline__ int swz_v<64>(int row) { return (row & 2) << 1; }
 
 __device__ __forceinline__ float wave_xor32(float x) {
     return __shfl_xor(x, 32, 64);
@@ -88,8 +106,11 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_bf16_kernel(
     float sl2, int n_qtiles, int total)
 {
     using C = Cfg<D>;
-    __shared__ __attribute__((aligned(16))) __bf16 sK[BN * C::KST];
-    __shared__ __attribute__((aligned(16))) __bf16 sV[D * C::VST];
+    // double-buffered K and V tiles, row-major, chunk-swizzled
+    __shared__ __attribute__((aligned(1024))) __bf16 sK0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) __bf16 sK1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) __bf16 sV0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) __bf16 sV1[C::TILE];
 
     // ---- work item: XCD-contiguous remap of the linear block id ----------
     const int L = blockIdx.x;
@@ -127,6 +148,20 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_bf16_kernel(
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) qf[s] = bf16x8{};
     }
+    // The softmax below works on raw scores with a positive factor sl2: a
+    // negative scale is applied by negating Q (exact in bf16), and a zero
+    // scale becomes 1e-30, for which exp2 of every visible score is exactly
+    // 1 (all weights equal, as with scale 0) while masked scores stay -inf.
+    if (sl2 < 0.f) {
+        sl2 = -sl2;
+#pragma unroll
+        for (int s = 0; s < C::KS; ++s) {
+            u32x4 x = __builtin_bit_cast(u32x4, qf[s]);
+            x ^= 0x80008000u;
+            qf[s] = __builtin_bit_cast(bf16x8, x);
+        }
+    }
+    sl2 = sl2 < 1e-30f ? 1e-30f : sl2;
 
     // ---- key range --------------------------------------------------------
     int kv_end = Nk;
@@ -139,149 +174,200 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_bf16_kernel(
 
     // per-lane limit of visible keys (inclusive)
     const int lim = CAUSAL ? ((qi + off) < (Nk - 1) ? (qi + off) : (Nk - 1)) : (Nk - 1);
-    const int wave_last_row = q0 + wave * 32 + 31;
+    const int wave_first_row = q0 + wave * 32;
 
-    // ---- staging registers ------------------------------------------------
-    u32x4 kreg[C::KLD];
-    u32x4 vreg[C::KPT];
-    const int va = tid % C::VA, vc = tid / C::VA;  // V staging: key group, column chunk
-
-    auto load_tile = [&](int j0) {
+    // ---- HBM -> LDS tile loads -------------------------------------------
+    // One wave-wide global_load_lds_dwordx4 fills RPW consecutive rows (1 KB):
+    // lane l lands at byte 16*l, i.e. row l / CH, chunk slot l % CH, and so
+    // fetches the chunk that the swizzle puts in that slot.  Rows past the end
+    // of K/V re-read the last row (finite data; those keys are masked).
+    const int ld_row = lane / C::CH, ld_slot = lane % C::CH;
+    auto dma_rows = [&](const __bf16 *base, int j0, __bf16 *dst, int is_v) {
 #pragma unroll
-        for (int i = 0; i < C::KLD; ++i) {
-            const int idx = tid + i * NTHR;
-            const int row = idx / C::CH, ch = idx % C::CH;
-            const int key = j0 + row;
-            kreg[i] = key < Nk ? *reinterpret_cast<const u32x4 *>(Kh + (size_t)key * D + ch * 8) : u32x4{};
-        }
-#pragma unroll
-        for (int r = 0; r < C::KPT; ++r) {
-            const int key = j0 + va * C::KPT + r;
-            vreg[r] = key < Nk ? *reinterpret_cast<const u32x4 *>(Vh + (size_t)key * D + vc * 8) : u32x4{};
-        }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int i = 0; i < C::KLD; ++i) {
-            const int idx = tid + i * NTHR;
-            const int row = idx / C::CH, ch = idx % C::CH;
-            *reinterpret_cast<u32x4 *>(sK + row * C::KST + ch * 8) = kreg[i];
-        }
-        const int pos = vperm(va * C::KPT);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int c = vc * 8 + e;
-            const int dw = e >> 1;
-            __bf16 *dst = sV + c * C::VST + pos;
-            if (C::KPT == 4) {
-                uint32_t x0, x1;
-                if (e & 1) {
-                    x0 = (vreg[0][dw] >> 16) | (vreg[1][dw] & 0xffff0000u);
-                    x1 = (vreg[2][dw] >> 16) | (vreg[3][dw] & 0xffff0000u);
-                } else {
-                    x0 = (vreg[0][dw] & 0xffffu) | (vreg[1][dw] << 16);
-                    x1 = (vreg[2][dw] & 0xffffu) | (vreg[3][dw] << 16);
-                }
-                *reinterpret_cast<u32x2 *>(dst) = u32x2{x0, x1};
-            } else {
-                uint32_t x0;
-                if (e & 1) x0 = (vreg[0][dw] >> 16) | (vreg[1][dw] & 0xffff0000u);
-                else x0 = (vreg[0][dw] & 0xffffu) | (vreg[1][dw] << 16);
-                *reinterpret_cast<uint32_t *>(dst) = x0;
-            }
+        for (int r = 0; r < C::ROUNDS; ++r) {
+            const int row0 = (r * 4 + wave) * C::RPW;  // first row of this wave's load
+            const int row = row0 + ld_row;
+            int key = j0 + row;
+            key = key < Nk ? key : Nk - 1;
+            const int slot = ld_slot ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
+            __builtin_amdgcn_global_load_lds(base + (size_t)key * D + slot * 8, (lds_void *)(dst + row0 * D), 16, 0,
+                                             0);
         }
     };
 
     // ---- running state ----------------------------------------------------
+    // m_ref: the reference subtracted before exp2, in units of
+    // t = s * scale * log2(e).  It is kept within RESCALE_TH of the running
+    // row max: raised (and O^T, l rescaled) only when a tile's max exceeds it
+    // by more than RESCALE_TH, so p = exp2(t - m_ref) <= 2^RESCALE_TH.
     f32x16 acc[C::CB];
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb) acc[cb] = f32x16{};
-    float m_run = -INFINITY;  // running max of t = s * scale * log2(e)
-    float l_run = 0.f;        // this lane's share of the denominator
+    float m_ref = -INFINITY;
+    float l_run = 0.f;  // this lane's share of the denominator
 
-    if (ntiles > 0) load_tile(0);
+    // lane constants of the transposing V reads: a 16-lane group reads keys
+    // [key0, key0 + 4) x columns [col0, col0 + 16); this lane's 8 bytes are key
+    // key0 + tr_key, columns col0 + tr_col .. + 3.
+    const int tr_grp = lane >> 4, tr_j = lane & 15;
+    const int tr_key = 4 * (tr_grp >> 1) + (tr_j >> 2);
+    const int tr_col = 16 * (tr_grp & 1) + 4 * (tr_j & 3);
 
-    for (int it = 0; it < ntiles; ++it) {
-        const int j0 = it * BN;
-        __syncthreads();  // previous tile fully consumed
-        store_tile();
-        __syncthreads();
-        if (it + 1 < ntiles) load_tile(j0 + BN);
-
-        if (CAUSAL && j0 > wave_last_row + off) continue;  // no row of this wave sees the tile
-
-        // S^T = K Q^T for two 32-key blocks
-        f32x16 st[2];
+    // K operand of score MFMA number i (i = 0..2*KS-1) of a tile; MFMAs
+    // alternate between the two 32-key halves (kt = i & 1, k-step i >> 1) so
+    // that consecutive MFMAs accumulate into different registers.
+    auto kfrag = [&](const __bf16 *sk, int i) {
+        const int kt = i & 1, s = i >> 1;
+        const int row = kt * 32 + n;
+        return *reinterpret_cast<const bf16x8 *>(sk + row * D + (((2 * s + g) ^ swz_k<D>(row)) * 8));
+    };
+    // V^T operand of PV MFMA (cb, kt, hh) from two transposing LDS reads:
+    // operand element i of lane (c, g) is key 16*hh + 32*kt + 4*g + i for
+    // i < 4 and + 8 + 4*g + (i - 4) for i >= 4, matching the keys of P^T.
+    auto vfrag = [&](const __bf16 *sv, int cb, int kt, int hh) {
+        i16x4 part[2];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            st[kt] = f32x16{};
-            const __bf16 *kp = sK + (kt * 32 + n) * C::KST + 8 * g;
-#pragma unroll
-            for (int s = 0; s < C::KS; ++s) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kp + 16 * s);
-                st[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st[kt], 0, 0, 0);
-            }
+        for (int half = 0; half < 2; ++half) {
+            const int key = kt * 32 + 16 * hh + 8 * half + tr_key;
+            const int col = cb * 32 + tr_col;
+            const __bf16 *p = sv + key * D + (((col >> 3) ^ swz_v<D>(key)) * 8) + (col & 7);
+            part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
         }
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    };
 
-        // scale (base 2) and mask
-        const bool need_mask = (j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > q0 + wave * 32 + off);
-        float mx = -INFINITY;
+    // Plain S^T = K Q^T of one tile (prologue only).
+    auto qk = [&](const __bf16 *sk, f32x16 (&st)[2]) {
+        st[0] = f32x16{};
+        st[1] = f32x16{};
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float x = st[kt][r] * sl2;
-                if (need_mask) {
-                    const int key = j0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (key > lim) x = -INFINITY;
-                }
-                st[kt][r] = x;
-                mx = fmaxf(mx, x);
-            }
-        }
-        mx = fmaxf(mx, wave_xor32(mx));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
+        for (int i = 0; i < 2 * C::KS; ++i)
+            st[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(sk, i), qf[i >> 1], st[i & 1], 0, 0, 0);
+    };
 
-        // P^T in bf16 (round to nearest even) for the MFMA; the denominator
-        // sums the unrounded fp32 values, so LSE carries no bf16 rounding.
-        u32x4 pb[2][2];
-        float psum = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float p0 = __builtin_amdgcn_exp2f(st[kt][8 * hh + 2 * i] - m_use);
-                    const float p1 = __builtin_amdgcn_exp2f(st[kt][8 * hh + 2 * i + 1] - m_use);
-                    const uint32_t pk = pack_bf16(p0, p1);
-                    pb[kt][hh][i] = pk;
-                    psum += p0 + p1;
-                }
-            }
-        }
-        l_run = l_run * alpha + psum;
+    // Software pipeline over key tiles j = 0 .. ntiles-1.  K and V have their
+    // own double-buffer rings; tile j's K sits in sK[j & 1], its V in
+    // sV[j & 1].  Iteration j feeds the MFMA units the scores of tile j+1
+    // while the vector ALUs turn the scores of tile j into P (the two streams
+    // are interleaved instruction by instruction below), then multiplies P by
+    // V of tile j.  Loads run ahead: iteration j starts K[j+2] and V[j+1]
+    // into the buffers iteration j-1 finished with.
+    auto kbuf = [&](int j) { return (j & 1) ? sK1 : sK0; };
+    auto vbuf = [&](int j) { return (j & 1) ? sV1 : sV0; };
+    auto dma_k = [&](int j) { dma_rows(Kh, j * BN, kbuf(j), 0); };
+    auto dma_v = [&](int j) { dma_rows(Vh, j * BN, vbuf(j), 1); };
 
-#pragma unroll
-        for (int cb = 0; cb < C::CB; ++cb) acc[cb] *= alpha;
+    // One pipeline iteration; cur holds S^T of tile j, nxt receives tile j+1.
+    // Returns false when this wave is done (its rows see no later key).
+    auto iteration = [&](const int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+        const int j0 = j * BN;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K[j+1] and V[j] have landed
+        __syncthreads();                                   // ... for every wave; K[j], V[j-1] are free
+        if (j + 2 < ntiles) dma_k(j + 2);
+        if (j + 1 < ntiles) dma_v(j + 1);
+        // waves whose rows see none of tile j skip it (and every later tile)
+        if (CAUSAL && j0 > wave_first_row + 31 + off) return;
 
-        // O^T += V^T P^T
-#pragma unroll
-        for (int cb = 0; cb < C::CB; ++cb) {
-            const __bf16 *vp = sV + (cb * 32 + n) * C::VST + 8 * g;
+        // mask (diagonal and end-of-K tiles only): raw score -> -inf
+        const bool need_mask = (j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > wave_first_row + off);
+        if (need_mask) {
+            const int rel = lim - j0 - 4 * g;  // key offset limit inside the tile for this lane
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vp + kt * 32 + 16 * hh);
-                    const bf16x8 bb = __builtin_bit_cast(bf16x8, pb[kt][hh]);
-                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc[cb], 0, 0, 0);
+                for (int r = 0; r < 16; ++r) {
+                    const int kk = kt * 32 + 8 * (r >> 2) + (r & 3);
+                    if (kk > rel) cur[kt][r] = -INFINITY;
                 }
             }
         }
+        // this lane's max over its 32 keys, in t units (sl2 > 0)
+        float mr = cur[0][0];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int r = (kt == 0 ? 1 : 0); r < 16; ++r) mr = fmaxf(mr, cur[kt][r]);
+        }
+        const float mloc = mr * sl2;
+
+        // raise the reference only when some row's max outgrew it
+        if (__builtin_amdgcn_ballot_w64(mloc > m_ref + RESCALE_TH) != 0) {
+            const float mp = fmaxf(mloc, wave_xor32(mloc));
+            const float m_new = fmaxf(m_ref, mp);
+            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb) acc[cb] *= alpha;
+            m_ref = m_new;
+        }
+        const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+
+        // scores of tile j+1 on the MFMA units, interleaved with P^T of tile j
+        // on the vector ALUs (bf16, round to nearest even; the denominator
+        // sums the unrounded fp32 values so LSE carries no bf16 rounding).
+        // The last iteration computes a discarded product of a stale buffer.
+        const __bf16 *skn = kbuf(j + 1);
+        constexpr int NQK = 2 * C::KS;  // score MFMAs per tile (8 or 16)
+        constexpr int PAIRS_PER = 16 / NQK;  // softmax pairs per score MFMA
+        u32x4 pb[2][2];
+        float psum = 0.f;
+        constexpr int KAHEAD = NQK < 6 ? NQK : 6;  // K operands in flight (LDS latency ~300 cycles)
+        bf16x8 kq[NQK];
+#pragma unroll
+        for (int i = 0; i < KAHEAD; ++i) kq[i] = kfrag(skn, i);
+        nxt[0] = f32x16{};
+        nxt[1] = f32x16{};
+#pragma unroll
+        for (int i = 0; i < NQK; ++i) {
+            if (i + KAHEAD < NQK) kq[i + KAHEAD] = kfrag(skn, i + KAHEAD);
+            nxt[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[i], qf[i >> 1], nxt[i & 1], 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < PAIRS_PER; ++q) {
+                const int pi = i * PAIRS_PER + q;  // pair index 0..15
+                const int kt = pi >> 3, hh = (pi >> 2) & 1, ii = pi & 3;
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[kt][8 * hh + 2 * ii], sl2, -m_use));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[kt][8 * hh + 2 * ii + 1], sl2, -m_use));
+                pb[kt][hh][ii] = pack_bf16(p0, p1);
+                psum += p0 + p1;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        l_run += psum;
+
+        // O^T += V^T P^T for tile j; cb innermost so consecutive MFMAs are
+        // independent; operands read two MFMAs ahead
+        const __bf16 *svc = vbuf(j);
+        constexpr int NPV = 4 * C::CB;   // PV MFMAs per tile (8 or 16)
+        constexpr int VAHEAD = 6;        // V operands in flight
+        bf16x8 vq[NPV];
+#pragma unroll
+        for (int i = 0; i < VAHEAD; ++i) vq[i] = vfrag(svc, i % C::CB, (i / C::CB) >> 1, (i / C::CB) & 1);
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+            const int cb = i % C::CB, kh = i / C::CB, kt = kh >> 1, hh = kh & 1;
+            if (i + VAHEAD < NPV) {
+                const int i2 = i + VAHEAD;
+                const int kh2 = i2 / C::CB;
+                vq[i2] = vfrag(svc, i2 % C::CB, kh2 >> 1, kh2 & 1);
+            }
+            acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[i], __builtin_bit_cast(bf16x8, pb[kt][hh]), acc[cb],
+                                                              0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    f32x16 stA[2], stB[2];
+    if (ntiles > 0) {
+        dma_k(0);
+        dma_v(0);
+        if (ntiles > 1) dma_k(1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        qk(sK0, stA);
+    }
+    for (int j = 0; j < ntiles; j += 2) {
+        iteration(j, stA, stB);
+        if (j + 1 < ntiles) iteration(j + 1, stB, stA);
     }
 
     // ---- epilogue: O = u / l, LSE = ln(sum exp(s)) -----------------------
@@ -301,7 +387,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_bf16_kernel(
         }
         if (LSE && g == 0)
             LSE[(size_t)(b * Hq + h) * Nq + qi] =
-                l_tot > 0.f ? (m_run + __log2f(l_tot)) * LN2 : -INFINITY;
+                l_tot > 0.f ? (m_ref + __log2f(l_tot)) * LN2 : -INFINITY;
     }
 }
 
