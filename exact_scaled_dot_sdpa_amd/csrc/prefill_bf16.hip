@@ -177,21 +177,29 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_bf16_kernel(
     const int wave_first_row = q0 + wave * 32;
 
     // ---- HBM -> LDS tile loads -------------------------------------------
-    // One wave-wide global_load_lds_dwordx4 fills RPW consecutive rows (1 KB):
-    // lane l lands at byte 16*l, i.e. row l / CH, chunk slot l % CH, and so
-    // fetches the chunk that the swizzle puts in that slot.  Rows past the end
-    // of K/V re-read the last row (finite data; those keys are masked).
-    const int ld_row = lane / C::CH, ld_slot = lane % C::CH;
-    auto dma_rows = [&](const __bf16 *base, int j0, __bf16 *dst, int is_v) {
+    // One wave-wide buffer_load_dwordx4 ... lds fills RPW consecutive rows
+    // (1 KB): lane l lands at byte 16*l, i.e. row l / CH, chunk slot l % CH,
+    // and fetches the chunk the swizzle puts in that slot.  Wave w fills rows
+    // (4r + w) * RPW .. + RPW - 1 in round r.  The buffer
+    // descriptor of each tile starts at the tile's first row and ends at the
+    // last row of K/V, so rows past the end read as zeros (hardware range
+    // check); no per-lane address arithmetic is left in the loop.
+    // The chunk swizzles of a loaded row do not depend on the round, so one
+    // lane offset per tensor serves every round; rounds step by a scalar
+    // offset (which the range check includes: out-of-range lanes write 0).
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int ld_row = wave * C::RPW + lane / C::CH, ld_slot = lane % C::CH;
+    const int ld_voff_k = (ld_row * D + ((ld_slot ^ swz_k<D>(ld_row)) * 8)) * 2;
+    const int ld_voff_v = (ld_row * D + ((ld_slot ^ swz_v<D>(ld_row)) * 8)) * 2;
+    constexpr int ROUND_BYTES = 4 * C::RPW * D * 2;
+    auto dma_rows = [&](const __bf16 *base, int j0, __bf16 *dst, int voff) {
+        const int rows_left = Nk - j0;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(base + (size_t)j0 * D), (short)0, (rows_left < BN ? rows_left : BN) * D * 2, 0x00020000);
 #pragma unroll
         for (int r = 0; r < C::ROUNDS; ++r) {
-            const int row0 = (r * 4 + wave) * C::RPW;  // first row of this wave's load
-            const int row = row0 + ld_row;
-            int key = j0 + row;
-            key = key < Nk ? key : Nk - 1;
-            const int slot = ld_slot ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
-            __builtin_amdgcn_global_load_lds(base + (size_t)key * D + slot * 8, (lds_void *)(dst + row0 * D), 16, 0,
-                                             0);
+            __bf16 *d = dst + (r * 4 + wave_s) * C::RPW * D;  // wave-uniform LDS destination
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)d, 16, voff, r * ROUND_BYTES, 0, 0);
         }
     };
 
@@ -213,13 +221,29 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_bf16_kernel(
     const int tr_key = 4 * (tr_grp >> 1) + (tr_j >> 2);
     const int tr_col = 16 * (tr_grp & 1) + 4 * (tr_j & 3);
 
+    // Lane offsets (elements) of the LDS operand reads, fixed for the whole
+    // kernel; everything else in a read address is a compile-time constant.
+    //   K: row n (+32 for the second key half; the swizzle of row n + 32 is
+    //      that of row n), chunk (2s + g) ^ swz.
+    int k_off[C::KS];
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) k_off[s] = n * D + (((2 * s + g) ^ swz_k<D>(n)) * 8);
+    //   V (transposing reads): key tr_key (+ 8*half + 16*hh + 32*kt, which
+    //      keeps key & 3), column block cb -> chunk ((cb ^ (swz >> 2)) << 2)
+    //      | (tr_col >> 3) when D = 128; the D = 64 swizzle is handled alike.
+    int v_off[C::CB];
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb) {
+        const int col = cb * 32 + tr_col;
+        v_off[cb] = tr_key * D + (((col >> 3) ^ swz_v<D>(tr_key)) * 8) + (col & 7);
+    }
+
     // K operand of score MFMA number i (i = 0..2*KS-1) of a tile; MFMAs
     // alternate between the two 32-key halves (kt = i & 1, k-step i >> 1) so
     // that consecutive MFMAs accumulate into different registers.
     auto kfrag = [&](const __bf16 *sk, int i) {
         const int kt = i & 1, s = i >> 1;
-        const int row = kt * 32 + n;
-        return *reinterpret_cast<const bf16x8 *>(sk + row * D + (((2 * s + g) ^ swz_k<D>(row)) * 8));
+        return *reinterpret_cast<const bf16x8 *>(sk + kt * 32 * D + k_off[s]);
     };
     // V^T operand of PV MFMA (cb, kt, hh) from two transposing LDS reads:
     // operand element i of lane (c, g) is key 16*hh + 32*kt + 4*g + i for
@@ -228,9 +252,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_bf16_kernel(
         i16x4 part[2];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            const int key = kt * 32 + 16 * hh + 8 * half + tr_key;
-            const int col = cb * 32 + tr_col;
-            const __bf16 *p = sv + key * D + (((col >> 3) ^ swz_v<D>(key)) * 8) + (col & 7);
+            const __bf16 *p = sv + (kt * 32 + 16 * hh + 8 * half) * D + v_off[cb];
             part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
         }
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
@@ -254,8 +276,8 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_bf16_kernel(
     // into the buffers iteration j-1 finished with.
     auto kbuf = [&](int j) { return (j & 1) ? sK1 : sK0; };
     auto vbuf = [&](int j) { return (j & 1) ? sV1 : sV0; };
-    auto dma_k = [&](int j) { dma_rows(Kh, j * BN, kbuf(j), 0); };
-    auto dma_v = [&](int j) { dma_rows(Vh, j * BN, vbuf(j), 1); };
+    auto dma_k = [&](int j) { dma_rows(Kh, j * BN, kbuf(j), ld_voff_k); };
+    auto dma_v = [&](int j) { dma_rows(Vh, j * BN, vbuf(j), ld_voff_v); };
 
     // One pipeline iteration; cur holds S^T of tile j, nxt receives tile j+1.
     // Returns false when this wave is done (its rows see no later key).
@@ -311,7 +333,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_bf16_kernel(
         constexpr int PAIRS_PER = 16 / NQK;  // softmax pairs per score MFMA
         u32x4 pb[2][2];
         float psum = 0.f;
-        constexpr int KAHEAD = NQK < 6 ? NQK : 6;  // K operands in flight (LDS latency ~300 cycles)
+        constexpr int KAHEAD = 4;  // K operands in flight (LDS latency ~300 cycles)
         bf16x8 kq[NQK];
 #pragma unroll
         for (int i = 0; i < KAHEAD; ++i) kq[i] = kfrag(skn, i);
@@ -338,7 +360,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_bf16_kernel(
         // independent; operands read two MFMAs ahead
         const __bf16 *svc = vbuf(j);
         constexpr int NPV = 4 * C::CB;   // PV MFMAs per tile (8 or 16)
-        constexpr int VAHEAD = 6;        // V operands in flight
+        constexpr int VAHEAD = 4;        // V operands in flight
         bf16x8 vq[NPV];
 #pragma unroll
         for (int i = 0; i < VAHEAD; ++i) vq[i] = vfrag(svc, i % C::CB, (i / C::CB) >> 1, (i / C::CB) & 1);
