@@ -27,10 +27,11 @@
 //     a 4-key x 16-column block and each lane receives 4 keys of one column,
 //     exactly the operand layout.  No transposed copy is ever stored.
 //   * Softmax in base 2: p = exp2(s * scale * log2 e - m), one FMA + v_exp_f32.
-//     The subtracted reference m is raised (and O^T, l rescaled) only when a
-//     row's max outgrows it by more than 2^8, which leaves u / l unchanged
-//     ("从注意力到 IO 感知执行", sec. 8: the subtracted value only changes the
-//     representation) and removes the per-tile rescale.
+//     The subtracted reference m is a past running max of the row; it is
+//     raised (and O^T, l rescaled) only when a tile's probabilities would
+//     exceed 2^24, which leaves u / l unchanged ("从注意力到 IO 感知执行",
+//     sec. 8: the subtracted value only changes the representation) and
+//     removes the per-tile row max and rescale from the common path.
 //   * Causal: tiles beyond the last visible key of the workgroup are never
 //     loaded; only tiles that straddle the diagonal (or the end of K) take the
 //     masked code path.  Bottom-right alignment: row i sees j <= i + Nk - Nq.
@@ -62,7 +63,10 @@ constexpr int BN = 64;   // keys per tile
 constexpr int NTHR = 256;
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float LOG2E = 1.44269504088896340736f;
-constexpr float RESCALE_TH = 8.f;  // reference lag allowed before O is rescaled (base-2 units)
+// A tile whose 32 probabilities (per lane) sum above 2^24 triggers the
+// rescale of the reference; below it every p <= 2^24, far from fp32 / bf16
+// range limits, and fp32 keeps its relative precision.
+constexpr float RESCALE_SUM = 16777216.f;
 
 template <int D>
 struct Cfg {
@@ -205,9 +209,8 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_bf16_kernel(
 
     // ---- running state ----------------------------------------------------
     // m_ref: the reference subtracted before exp2, in units of
-    // t = s * scale * log2(e).  It is kept within RESCALE_TH of the running
-    // row max: raised (and O^T, l rescaled) only when a tile's max exceeds it
-    // by more than RESCALE_TH, so p = exp2(t - m_ref) <= 2^RESCALE_TH.
+    // t = s * scale * log2(e): a past running max of the row, raised (with O^T
+    // and l rescaled) only when a tile's probabilities would outgrow it.
     f32x16 acc[C::CB];
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb) acc[cb] = f32x16{};
@@ -303,37 +306,22 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_bf16_kernel(
                 }
             }
         }
-        // this lane's max over its 32 keys, in t units (sl2 > 0)
-        float mr = cur[0][0];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-            for (int r = (kt == 0 ? 1 : 0); r < 16; ++r) mr = fmaxf(mr, cur[kt][r]);
-        }
-        const float mloc = mr * sl2;
-
-        // raise the reference only when some row's max outgrew it
-        if (__builtin_amdgcn_ballot_w64(mloc > m_ref + RESCALE_TH) != 0) {
-            const float mp = fmaxf(mloc, wave_xor32(mloc));
-            const float m_new = fmaxf(m_ref, mp);
-            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-            l_run *= alpha;
-#pragma unroll
-            for (int cb = 0; cb < C::CB; ++cb) acc[cb] *= alpha;
-            m_ref = m_new;
-        }
-        const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-
-        // scores of tile j+1 on the MFMA units, interleaved with P^T of tile j
+        // Scores of tile j+1 on the MFMA units, interleaved with P^T of tile j
         // on the vector ALUs (bf16, round to nearest even; the denominator
         // sums the unrounded fp32 values so LSE carries no bf16 rounding).
+        // P uses the current reference m_ref, a past running max; only when
+        // some p would exceed 2^24 (the tile's exp sum tells) is the reference
+        // raised to the running max, O^T and l rescaled and P recomputed.  The
+        // first tile always takes that path.  Masked scores are -inf (p = 0).
         // The last iteration computes a discarded product of a stale buffer.
         const __bf16 *skn = kbuf(j + 1);
-        constexpr int NQK = 2 * C::KS;  // score MFMAs per tile (8 or 16)
+        constexpr int NQK = 2 * C::KS;       // score MFMAs per tile (8 or 16)
         constexpr int PAIRS_PER = 16 / NQK;  // softmax pairs per score MFMA
+        constexpr int KAHEAD = 4;            // K operands in flight
         u32x4 pb[2][2];
-        float psum = 0.f;
-        constexpr int KAHEAD = 4;  // K operands in flight (LDS latency ~300 cycles)
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};
+        const bool fresh = __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) != 0;
+        const float m_use = fresh ? 0.f : m_ref;
         bf16x8 kq[NQK];
 #pragma unroll
         for (int i = 0; i < KAHEAD; ++i) kq[i] = kfrag(skn, i);
@@ -350,9 +338,41 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_bf16_kernel(
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[kt][8 * hh + 2 * ii], sl2, -m_use));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[kt][8 * hh + 2 * ii + 1], sl2, -m_use));
                 pb[kt][hh][ii] = pack_bf16(p0, p1);
-                psum += p0 + p1;
+                ps[ii] += p0 + p1;
             }
             __builtin_amdgcn_sched_barrier(0);
+        }
+        float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        if (fresh || __builtin_amdgcn_ballot_w64(!(psum <= RESCALE_SUM)) != 0) {  // rare
+            float mr = cur[0][0];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+                for (int r = (kt == 0 ? 1 : 0); r < 16; ++r) mr = fmaxf(mr, cur[kt][r]);
+            }
+            const float mloc = mr * sl2;
+            const float mp = fmaxf(mloc, wave_xor32(mloc));
+            const float m_new = fmaxf(m_ref, mp);
+            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb) acc[cb] *= alpha;
+            m_ref = m_new;
+            const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
+            psum = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) {
+                        const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[kt][8 * hh + 2 * ii], sl2, -mu));
+                        const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[kt][8 * hh + 2 * ii + 1], sl2, -mu));
+                        pb[kt][hh][ii] = pack_bf16(p0, p1);
+                        psum += p0 + p1;
+                    }
+                }
+            }
         }
         l_run += psum;
 
@@ -415,11 +435,11 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_bf16_kernel(
 
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs &a, hipStream_t stream) {
+    const float sl2 = a.scale * LOG2E;
     const int n_qtiles = (a.Nq + BM - 1) / BM;
     const long long total = (long long)a.B * a.Hq * n_qtiles;
     if (total <= 0) return hipSuccess;
     if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const float sl2 = a.scale * LOG2E;
     hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), dim3((unsigned)total), dim3(NTHR), 0, stream,
                        (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v, (__bf16 *)a.o,
                        a.lse, a.Hq, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles, (int)total);
