@@ -59,10 +59,10 @@ def stored_traffic(kernel):
         return None
     from exact_scaled_dot_sdpa_amd.build import source_digest
 
-    if t.get("kernel_source_digest") != source_digest():
-        return None
     e = t.get("kernels", {}).get(kernel)
-    return None if e is None else e.get("bytes_per_launch")
+    if e is None or e.get("source_digest") != source_digest(kernel):
+        return None
+    return e.get("bytes_per_launch")
 
 
 def cpu_baseline(q, k, v, w, target_s):

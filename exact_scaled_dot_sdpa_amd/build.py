@@ -24,14 +24,25 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def source_digest() -> str:
-    """Digest of the kernel sources (csrc/*.hip, *.h).  Stored hardware-counter
-    figures carry it, so that figures taken on other kernels are not reused."""
+# The sources each logical kernel is built from (csrc/ file names).
+KERNEL_SOURCES = {
+    "prefill": ("prefill_bf16.hip", "kernels.h"),
+    "decode": ("decode_bf16.hip", "kernels.h"),
+}
+
+
+def source_digest(kernel=None) -> str:
+    """Digest of the kernel sources: all of csrc/*.hip, *.h, or only those of
+    one logical kernel ("prefill", "decode").  Stored hardware-counter figures
+    carry it, so that figures taken on other kernels are not reused."""
+    if kernel is None:
+        names = [n for n in sorted(os.listdir(CSRC)) if n.endswith((".hip", ".h"))]
+    else:
+        names = sorted(KERNEL_SOURCES[kernel])
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in names:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 

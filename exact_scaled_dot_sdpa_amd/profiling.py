@@ -9,8 +9,8 @@ into a short table.  `traffic` turns two `rocprofv3 --pmc FETCH_SIZE` /
 `--pmc WRITE_SIZE` counter files (KiB per dispatch) into HBM bytes per launch:
 each counter is scaled by the factor that makes the plain device copy of
 --calib-mib MiB (launched by `bench.py --calib-copy-mib`) read and write
-exactly that many bytes.  The JSON records the kernel-source digest; bench.py
-reports the bytes only while the kernels are unchanged.
+exactly that many bytes.  The JSON records each kernel's source digest;
+bench.py reports a kernel's bytes only while its sources are unchanged.
 """
 import argparse
 import csv
@@ -94,7 +94,8 @@ def traffic(fetch_csv, write_csv, calib_mib, cmd_fetch, cmd_write, json_out, out
         read_b = fk * f_fac * 1024.0
         write_b = wk * w_fac * 1024.0
         kernels[logical] = {"bytes_per_launch": int(round(read_b + write_b)), "read_bytes": int(round(read_b)),
-                            "write_bytes": int(round(write_b)), "parts": detail}
+                            "write_bytes": int(round(write_b)), "source_digest": source_digest(logical),
+                            "parts": detail}
     doc = {
         "kernel_source_digest": source_digest(),
         "calibration": {"copy_mib": calib_mib, "fetch_kib_raw": f_raw, "write_kib_raw": w_raw,
@@ -110,11 +111,10 @@ def traffic(fetch_csv, write_csv, calib_mib, cmd_fetch, cmd_write, json_out, out
              "Calibration: one plain device copy of %d MiB reads %.1f KiB by FETCH_SIZE and writes %.1f KiB by "
              "WRITE_SIZE, so FETCH_SIZE is scaled by %.4f and WRITE_SIZE by %.4f." % (
                  calib_mib, f_raw, w_raw, f_fac, w_fac), "",
-             "Kernel-source digest: `%s`" % doc["kernel_source_digest"], "",
-             "| kernel | read (MB) | write (MB) | total (MB) |", "|---|---|---|---|"]
+             "| kernel | read (MB) | write (MB) | total (MB) | source digest |", "|---|---|---|---|---|"]
     for k, e in kernels.items():
-        lines.append("| %s | %.2f | %.2f | %.2f |" % (k, e["read_bytes"] / 1e6, e["write_bytes"] / 1e6,
-                                                      e["bytes_per_launch"] / 1e6))
+        lines.append("| %s | %.2f | %.2f | %.2f | `%s` |" % (k, e["read_bytes"] / 1e6, e["write_bytes"] / 1e6,
+                                                             e["bytes_per_launch"] / 1e6, e["source_digest"]))
     text = "\n".join(lines) + "\n"
     with open(out, "w") as f:
         f.write(text)
