@@ -10,32 +10,53 @@
 
 namespace {
 
-constexpr int DEFAULT_KEYS_PER_SPLIT = 256;
+// Upper bound on the workgroups of the decode split kernel; the default
+// (keys_per_split == 0) uses as many as the device holds at once, at most this.
+constexpr int DECODE_MAX_WG = 2048;
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 bool supported_d(int d) { return d == 64 || d == 128; }
 
-bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+struct DecodePlan {
+    int nhb;     // blocks of up to 16 query heads per K/V head
+    int gb;      // heads per partial-result slot: min(G, 16)
+    int n_wg;    // split-kernel workgroups (0 = device default)
+    int max_wg;  // workgroups the workspace is sized for
+    long long slots;
+};
 
-int effective_kps(int keys_per_split) {
-    return keys_per_split == 0 ? DEFAULT_KEYS_PER_SPLIT : keys_per_split;
+// Sizes are valid and non-negative here.
+DecodePlan decode_plan(int B, int Hq, int Hkv, int max_seq_len, int keys_per_split) {
+    DecodePlan p;
+    const int G = Hq / Hkv;
+    p.nhb = (G + 15) / 16;
+    p.gb = G < 16 ? G : 16;
+    if (keys_per_split > 0) {
+        const long long keys = (long long)B * Hkv * p.nhb * max_seq_len;
+        long long n = (keys + keys_per_split - 1) / keys_per_split;
+        n = n < 1 ? 1 : (n > DECODE_MAX_WG ? DECODE_MAX_WG : n);
+        p.n_wg = (int)n;
+        p.max_wg = (int)n;
+    } else {
+        p.n_wg = 0;
+        p.max_wg = DECODE_MAX_WG;
+    }
+    p.slots = (long long)B * Hkv * p.nhb + p.max_wg - 1;
+    return p;
 }
 
-bool valid_kps(int kps) { return kps >= 64 && kps <= 65536 && kps % 64 == 0; }
-
-long long n_splits_for(int max_seq_len, int kps) {
-    const long long s = ((long long)max_seq_len + kps - 1) / kps;
-    return s < 1 ? 1 : s;
-}
-
-// fp32 partial outputs [B,Hq,S,d], then (256-byte aligned) partial LSEs [B,Hq,S]
-void workspace_layout(int B, int Hq, int d, long long S, size_t *o_bytes, size_t *total) {
-    const size_t rows = (size_t)B * Hq * (size_t)S;
+// fp32 partial outputs [slots, gb, d], then (256-byte aligned) partial LSEs [slots, gb]
+void workspace_layout(const DecodePlan &p, int d, size_t *o_bytes, size_t *total) {
+    const size_t rows = (size_t)p.slots * p.gb;
     size_t ob = rows * (size_t)d * sizeof(float);
     ob = (ob + 255) & ~(size_t)255;
     *o_bytes = ob;
     *total = ob + rows * sizeof(float);
+}
+
+bool decode_sizes_ok(int B, int Hq, int Hkv, int max_seq_len) {
+    return B >= 0 && Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0 && max_seq_len >= 0;
 }
 
 }  // namespace
@@ -68,11 +89,9 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_seq_len, int d, int keys_per_split)
 {
-    const int kps = effective_kps(keys_per_split);
-    if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_seq_len < 0 || !supported_d(d) || !valid_kps(kps))
-        return 0;
+    if (!decode_sizes_ok(B, Hq, Hkv, max_seq_len) || !supported_d(d) || keys_per_split < 0) return 0;
     size_t ob, total;
-    workspace_layout(B, Hq, d, n_splits_for(max_seq_len, kps), &ob, &total);
+    workspace_layout(decode_plan(B, Hq, Hkv, max_seq_len, keys_per_split), d, &ob, &total);
     return total;
 }
 
@@ -80,27 +99,28 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, const i
                 float *lse, int B, int Hq, int Hkv, int max_seq_len, int d, float scale, int keys_per_split,
                 int dtype, void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_seq_len < 0) return ATTN_ERR_INVALID_ARG;
+    if (!decode_sizes_ok(B, Hq, Hkv, max_seq_len)) return ATTN_ERR_INVALID_ARG;
     if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
-    const int kps = effective_kps(keys_per_split);
-    if (!valid_kps(kps)) return ATTN_ERR_INVALID_ARG;
-    if (!supported_d(d) || dtype != ATTN_BF16 || !supported_group(Hq / Hkv)) return ATTN_ERR_UNSUPPORTED;
+    if (keys_per_split < 0) return ATTN_ERR_INVALID_ARG;
+    if (!supported_d(d) || dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
     if (B == 0) return ATTN_OK;
     if (!q || !o || !seq_lens || (max_seq_len > 0 && (!k_cache || !v_cache))) return ATTN_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(o, 16) || !aligned(seq_lens, 4) || (k_cache && !aligned(k_cache, 16)) ||
         (v_cache && !aligned(v_cache, 16)))
         return ATTN_ERR_INVALID_ARG;
     if (lse && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARG;
-    const long long S = n_splits_for(max_seq_len, kps);
-    if (S > 65535 || Hkv > 65535 || B > 65535) return ATTN_ERR_UNSUPPORTED;  // grid y/z limits
-    if ((long long)B * Hkv * max_seq_len > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+    const DecodePlan p = decode_plan(B, Hq, Hkv, max_seq_len, keys_per_split);
+    // cache rows and segment counts stay in 32-bit arithmetic
+    if ((long long)B * Hkv * max_seq_len > 0x7fffffffLL || (long long)B * Hq > 0x7fffffffLL ||
+        p.slots > 0x7fffffffLL)
+        return ATTN_ERR_UNSUPPORTED;
     size_t ob, need;
-    workspace_layout(B, Hq, d, S, &ob, &need);
+    workspace_layout(p, d, &ob, &need);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_ERR_WORKSPACE;
 
-    attn::DecodeArgs a{q, k_cache, v_cache, seq_lens, o, lse, B, Hq, Hkv, max_seq_len, d, scale, kps, (int)S,
-                       (float *)workspace, (float *)((char *)workspace + ob)};
+    attn::DecodeArgs a{q, k_cache, v_cache, seq_lens, o, lse, B, Hq, Hkv, max_seq_len, d, scale,
+                       p.nhb, p.n_wg, p.max_wg, (float *)workspace, (float *)((char *)workspace + ob)};
     const hipError_t e = attn::launch_decode_bf16(a, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }

@@ -1,28 +1,48 @@
-// decode_bf16.hip -- one-token decode against a bf16 KV cache (split-KV).
+// decode_bf16.hip -- one-token decode against a bf16 KV cache.
 //
 // Each query of the new token attends to the first seq_lens[b] cached rows of
 // its K/V head ("Transformer 笔记：注意力机制为什么会变成系统问题", KV-cache
-// section).  The work is HBM-bound (about 4 FLOP per cache byte), so the
-// kernels are built around streaming the valid cache rows exactly once:
+// section).  The work is HBM-bound (about 4 FLOP per cache byte for four query
+// heads per K/V head), so the design streams every valid cache row exactly
+// once, keeps enough of them in flight to cover the memory latency, and keeps
+// the per-byte instruction count low enough that the vector ALUs never become
+// the limit.
 //
-//   split kernel  grid (split, KV head, sequence).  A workgroup streams its
-//                 split's K and V rows with 16-byte loads (a row of d bf16 is
-//                 d/8 lanes), serves all G = Hq/Hkv query heads of the group
-//                 from each row it loads, and keeps for every head the running
-//                 reference m, denominator l and un-normalised accumulator of
-//                 the online softmax ("从注意力到 IO 感知执行", sec. 8, eqs.
-//                 (1)-(2)).  The reference is raised only when a score exceeds
-//                 it by more than 2^8 (in base 2), which leaves u / l exact
-//                 (the same sec. 8 notes that the subtracted value only changes
-//                 the representation) and skips almost every rescale.  Lanes
-//                 handling different keys merge their states at the end of the
-//                 split; the split's normalised partial output and its
-//                 log-sum-exp go to the workspace.
-//   merge kernel  grid (sequence * query head): lse = ln sum_s exp(lse_s),
-//                 o = sum_s exp(lse_s - lse) o_s, which is one more step of the
-//                 same recurrence applied to whole splits.
+// Work partition.  A (sequence b, K/V head hk, block hb of up to 16 query heads
+// of the group) is one "segment" of seq_lens[b] keys; the segments are laid
+// end to end (b outer, then hk, then hb) into one list of T keys, which is cut
+// into n_wg equal ranges, one per single-wave workgroup.  With n_wg set to the
+// number of workgroups the chip holds at once, every workgroup streams the
+// same number of bytes whatever the length mix of the batch.  A range that
+// covers part of a segment produces a partial result (normalised output and
+// log-sum-exp of its keys); the merge kernel combines the partials of each
+// segment, which is one more step of the online-softmax recurrence
+// ("从注意力到 IO 感知执行", sec. 8, eqs. (1)-(2)) applied to whole ranges.
+// Every workgroup computes the segment prefix sums itself from seq_lens (a
+// 64-lane scan per 64 sequences); no planning kernel runs first.
 //
-// Cache rows at or beyond seq_lens[b] are never loaded.
+// gfx950 mapping inside a workgroup (one wave):
+//   * The range is walked in chunks of 32 keys (fewer at the end of a segment
+//     or range).  The K and V rows of a chunk, and the query rows of its
+//     segment, go from HBM straight into LDS with buffer_load ... lds (1 KB per
+//     instruction); a ring of NST stages keeps NST-1 chunks in flight while one
+//     is computed.  The buffer descriptor of each load ends at the last valid
+//     row, so rows at or beyond seq_lens[b] are never read: the hardware range
+//     check returns zeros for them.
+//   * Scores S = K Q^T on v_mfma_f32_16x16x32_bf16: the 16 keys of a half-chunk
+//     are the M dimension and the (up to 16) query heads the N dimension, so
+//     each lane ends up with 4 scores of one head; no cross-lane reduction is
+//     needed for the dot products.
+//   * Softmax in base 2 with a lazily raised reference, as in the prefill
+//     kernel: the first chunk of a range sets the reference to its maximum;
+//     later chunks only check that their probabilities stay below 2^24 and
+//     rescale in the rare case they do not.
+//   * P^T (bf16, in registers, exactly the B-operand layout) times V^T: the
+//     A operand is read from the row-major V chunk with ds_read_b64_tr_b16,
+//     so no transposed copy is stored.  O^T accumulates in 8 (d = 128) or 4
+//     (d = 64) 16x16 fp32 tiles.
+//   * LDS rows are XOR-swizzled per 16-byte chunk so that both operand reads
+//     are free of bank conflicts.
 #include "kernels.h"
 
 #include <math.h>
@@ -30,238 +50,517 @@
 namespace attn {
 namespace {
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int NTHR = 256;
-constexpr int NWAVE = 4;
-constexpr int UNROLL = 4;        // key rows per lane per step
-constexpr float RESCALE_TH = 8.f;  // raise the reference when a score exceeds it by 2^8
+constexpr int CK = 32;  // keys per chunk
+#ifndef ATTN_DECODE_STAGES
+#define ATTN_DECODE_STAGES 3
+#endif
+constexpr int DECODE_STAGES = ATTN_DECODE_STAGES;  // LDS ring depth (chunks)
+static_assert(DECODE_STAGES >= 2 && DECODE_STAGES <= 4, "pipeline depth");
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr float LOG2E = 1.44269504088896340736f;
+// A chunk whose (per lane, 8) probabilities sum above 2^24 raises the
+// reference; below it every p <= 2^24 and fp32 keeps its relative precision.
+constexpr float RESCALE_SUM = 16777216.f;
 
-__device__ __forceinline__ float dpp_f(float x, int ctrl_sel) {
-    const int xi = __builtin_bit_cast(int, x);
-    int r;
-    switch (ctrl_sel) {
-        case 0: r = __builtin_amdgcn_mov_dpp(xi, 0xB1, 0xf, 0xf, false); break;   // quad xor 1
-        case 1: r = __builtin_amdgcn_mov_dpp(xi, 0x4E, 0xf, 0xf, false); break;   // quad xor 2
-        case 2: r = __builtin_amdgcn_mov_dpp(xi, 0x141, 0xf, 0xf, false); break;  // mirror within 8
-        default: r = __builtin_amdgcn_mov_dpp(xi, 0x140, 0xf, 0xf, false); break; // mirror within 16
+template <int D>
+struct DC {
+    static constexpr int CH = D / 8;                // 16-byte chunks per row
+    static constexpr int RPI = 64 / CH;             // rows per 1 KB load instruction
+    static constexpr int KI = CK / RPI;             // load instructions per K (or V) chunk
+    static constexpr int PER = 16 / RPI;            // instructions after which the swizzle repeats
+    static constexpr int KS = D / 32;               // k-steps of the score MFMA
+    static constexpr int CB = D / 16;               // 16-column blocks of O^T
+    static constexpr int CHUNK_BYTES = CK * D * 2;  // one K or V chunk
+};
+
+// Stage layout in LDS: K chunk, V chunk, query rows of the chunk's segment.
+template <int D, int QR>
+struct Stage {
+    using C = DC<D>;
+    static constexpr int QROWS = (QR + C::RPI - 1) / C::RPI * C::RPI;
+    static constexpr int QI = QROWS / C::RPI;  // load instructions for the query rows
+    static constexpr int K_OFF = 0;
+    static constexpr int V_OFF = C::CHUNK_BYTES;
+    static constexpr int Q_OFF = 2 * C::CHUNK_BYTES;
+    static constexpr int BYTES = Q_OFF + QROWS * D * 2;
+    static constexpr int NI = 2 * C::KI + QI;  // load instructions per chunk
+    static_assert(BYTES % 1024 == 0, "stage alignment");
+    static_assert((QROWS & (QROWS - 1)) == 0 && QROWS <= 16, "query rows: power of two up to 16");
+};
+
+// XOR swizzles of the 16-byte chunk index within a row (see the operand reads
+// for the access patterns they serve).
+template <int D> __device__ __forceinline__ int swz_k(int row);
+template <> __device__ __forceinline__ int swz_k<128>(int row) { return row & 15; }
+template <> __device__ __forceinline__ int swz_k<64>(int row) { return (row >> 1) & 7; }
+template <int D> __device__ __forceinline__ int swz_v(int row);
+template <> __device__ __forceinline__ int swz_v<128>(int row) { return (row & 7) << 1; }
+template <> __device__ __forceinline__ int swz_v<64>(int row) { return ((row >> 1) & 3) << 1; }
+
+__device__ __forceinline__ int clamp_len(int L, int Lmax) { return L < 0 ? 0 : (L > Lmax ? Lmax : L); }
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
     }
-    return __builtin_bit_cast(float, r);
-}
-
-// Sum over the CH lanes that hold one cache row (CH = 8 or 16, aligned groups).
-template <int CH>
-__device__ __forceinline__ float row_sum(float x) {
-    x += dpp_f(x, 0);
-    x += dpp_f(x, 1);
-    x += dpp_f(x, 2);
-    if (CH == 16) x += dpp_f(x, 3);
     return x;
 }
 
-// Dot product of 8 bf16 pairs (packed two per dword), fp32 accumulation.
-// The dwords are copied to scalars before the bit cast: a bit cast applied
-// directly to a subscripted ext_vector element is miscompiled by this clang
-// (every subscript reads element 0).
-__device__ __forceinline__ float dot8(u32x4 q, u32x4 k) {
-    const uint32_t qa[4] = {q.x, q.y, q.z, q.w}, ka[4] = {k.x, k.y, k.z, k.w};
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t qq = qa[i], kk = ka[i];
-        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qq), __builtin_bit_cast(bf16x2, kk), s, false);
-    }
-    return s;
+// Round-to-nearest-even pair conversion fp32 -> packed bf16 (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(NTHR) void decode_split_kernel(
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Sum over the keys of the whole batch, in units of keys x segments:
+// T = nsub * sum_b clamp(seq_lens[b]).  Wave-uniform.
+__device__ __forceinline__ long long total_keys(const int32_t *seq_lens, int B, int Lmax, int nsub, int lane) {
+    long long t = 0;
+    for (int pb = 0; pb < B; pb += 64) {
+        const int L = pb + lane < B ? clamp_len(seq_lens[pb + lane], Lmax) : 0;
+        const int s = wave_incl_scan(L, lane);
+        t += __builtin_amdgcn_readlane(s, 63);
+    }
+    return t * nsub;
+}
+
+// First key position of workgroup w's range: floor(w * T / n_wg).
+__device__ __forceinline__ long long range_start(long long w, long long T, int n_wg) { return w * T / n_wg; }
+
+// Loads of one chunk into a stage: K and V rows (kv_bytes of them are in
+// range, the rest of the chunk reads as zeros) and the query rows of the
+// segment (q_bytes in range).  voff_*: per-lane byte offsets within a 1 KB
+// load, one per swizzle phase.
+template <int D, int QR>
+__device__ __forceinline__ void dma_chunk(char *dst, const __bf16 *k, const __bf16 *v, const __bf16 *q, int kv_bytes,
+                                          int q_bytes, const int (&voff_k)[DC<D>::PER],
+                                          const int (&voff_v)[DC<D>::PER]) {
+    using C = DC<D>;
+    using S = Stage<D, QR>;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)k, (short)0, kv_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)v, (short)0, kv_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)q, (short)0, q_bytes, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < C::KI; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(dst + S::K_OFF + i * 1024), 16, voff_k[i % C::PER],
+                                                 i * 1024, 0, 0);
+#pragma unroll
+    for (int i = 0; i < C::KI; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(dst + S::V_OFF + i * 1024), 16, voff_v[i % C::PER],
+                                                 i * 1024, 0, 0);
+#pragma unroll
+    for (int i = 0; i < S::QI; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void *)(dst + S::Q_OFF + i * 1024), 16, voff_k[i % C::PER],
+                                                 i * 1024, 0, 0);
+}
+
+template <int D, int QR, int NST>
+__global__ __launch_bounds__(64) void decode_chunk_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ Kc, const __bf16 *__restrict__ Vc,
-    const int32_t *__restrict__ seq_lens, float *__restrict__ ws_o, float *__restrict__ ws_lse, int Hq,
-    int Hkv, int Lmax, int kps, int n_splits, float sl2)
+    const int32_t *__restrict__ seq_lens, float *__restrict__ ws_o, float *__restrict__ ws_lse, int B, int Hq,
+    int Hkv, int Lmax, int nhb, int n_wg, float sl2)
 {
-    constexpr int CH = D / 8;    // lanes per cache row
-    constexpr int KW = 64 / CH;  // rows per wave-wide load
-    __shared__ float s_acc[NWAVE][G][D];
-    __shared__ float s_m[NWAVE][G];
-    __shared__ float s_l[NWAVE][G];
+    using C = DC<D>;
+    using S = Stage<D, QR>;
+    extern __shared__ __attribute__((aligned(1024))) char lds[];
 
-    const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
-    int L = seq_lens[b];
-    L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
-    const int k_begin = split * kps;
-    if (k_begin >= L) return;  // empty split: the merge kernel never reads it
-    const int k_end = (k_begin + kps < L) ? k_begin + kps : L;
+    const int lane = threadIdx.x;
+    const int w = blockIdx.x;
+    const int G = Hq / Hkv;
+    const int GB = G < 16 ? G : 16;  // heads per partial-result slot
+    const int nsub = Hkv * nhb;      // segments per sequence
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int sub = lane / CH, ch = lane % CH;
+    // ---- this workgroup's key range [a0, a1) -----------------------------
+    const long long T = total_keys(seq_lens, B, Lmax, nsub, lane);
+    const long long a0 = range_start(w, T, n_wg), a1 = range_start(w + 1, T, n_wg);
+    if (a0 >= a1) return;
 
-    const size_t head_row0 = (size_t)(b * Hkv + hk) * Lmax;
-    const __bf16 *Kh = Kc + head_row0 * D + ch * 8;
-    const __bf16 *Vh = Vc + head_row0 * D + ch * 8;
+    // locate a0: sequence b (page pb, lane f), segment sub, key
+    int pb = 0, f = 0, pageL = 0;
+    long long bstart = 0;
+    for (;; pb += 64) {  // a0 < T, so some page holds it
+        pageL = pb + lane < B ? clamp_len(seq_lens[pb + lane], Lmax) : 0;
+        const int incl = wave_incl_scan(pageL, lane);
+        const long long end_i = bstart + (long long)incl * nsub;
+        const unsigned long long hit = __builtin_amdgcn_ballot_w64(end_i > a0);
+        if (hit) {
+            f = __builtin_ctzll(hit);
+            bstart += (long long)(__builtin_amdgcn_readlane(incl, f) - __builtin_amdgcn_readlane(pageL, f)) * nsub;
+            break;
+        }
+        bstart += (long long)__builtin_amdgcn_readlane(incl, 63) * nsub;
+    }
+    int b = pb + f;
+    int Lb = __builtin_amdgcn_readlane(pageL, f);
+    int sub, key;
+    {
+        const long long off = a0 - bstart;
+        sub = (int)(off / Lb);
+        key = (int)(off - (long long)sub * Lb);
+    }
+    long long pos = a0;
+    bool piece_start = true;
 
-    u32x4 qv[G];
+    // ---- scale: positive factor sl2 (negative scale: negate Q) ------------
+    const bool neg = sl2 < 0.f;
+    sl2 = neg ? -sl2 : sl2;
+    sl2 = sl2 < 1e-30f ? 1e-30f : sl2;
+
+    // ---- DMA lane offsets (bytes within one 1 KB load) --------------------
+    const int ld_q = lane / C::CH, ld_p = lane % C::CH;
+    int voff_k[C::PER], voff_v[C::PER];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-        qv[hh] = *reinterpret_cast<const u32x4 *>(Q + ((size_t)(b * Hq + hk * G + hh)) * D + ch * 8);
-
-    float m[G], l[G], acc[G][8];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        m[hh] = -INFINITY;
-        l[hh] = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+    for (int i = 0; i < C::PER; ++i) {
+        const int R = i * C::RPI + ld_q;
+        voff_k[i] = ld_q * D * 2 + ((ld_p ^ swz_k<D>(R)) * 16);
+        voff_v[i] = ld_q * D * 2 + ((ld_p ^ swz_v<D>(R)) * 16);
     }
 
-    constexpr int WSTEP = UNROLL * KW;     // rows per wave per step
-    constexpr int BSTEP = NWAVE * WSTEP;   // rows per workgroup per step
-    for (int base = k_begin + wave * WSTEP; base < k_end; base += BSTEP) {
-        u32x4 kr[UNROLL], vr[UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int key = base + u * KW + sub;
-            if (key < k_end) {
-                kr[u] = *reinterpret_cast<const u32x4 *>(Kh + (size_t)key * D);
-                vr[u] = *reinterpret_cast<const u32x4 *>(Vh + (size_t)key * D);
-            } else {
-                kr[u] = u32x4{};
-                vr[u] = u32x4{};
+    // per-stage chunk records (wave-uniform)
+    int m_seg[NST], m_cnt[NST], m_gblk[NST];
+    bool m_first[NST], m_last[NST];
+
+    // Issue the loads of the next chunk of the range into stage st and
+    // advance the cursor; false (nothing issued) once the range is done.
+    auto issue = [&](const int st) {
+        if (pos >= a1) return false;
+        const long long left = a1 - pos;
+        int cnt = Lb - key;
+        cnt = cnt < CK ? cnt : CK;
+        cnt = left < cnt ? (int)left : cnt;
+        if (cnt <= 0) {  // cannot happen for a consistent walk; ends it rather than spin
+            pos = a1;
+            return false;
+        }
+        const int hk = sub / nhb, hb = sub - hk * nhb;
+        const int gblk = G - 16 * hb < 16 ? G - 16 * hb : 16;
+        const size_t row0 = (size_t)(b * Hkv + hk) * Lmax + key;
+        dma_chunk<D, QR>(lds + st * S::BYTES, Kc + row0 * D, Vc + row0 * D,
+                         Q + ((size_t)b * Hq + hk * G + 16 * hb) * D, cnt * D * 2, gblk * D * 2, voff_k, voff_v);
+        m_seg[st] = b * nsub + sub;
+        m_cnt[st] = cnt;
+        m_gblk[st] = gblk;
+        m_first[st] = piece_start;
+        m_last[st] = (key + cnt == Lb) || (pos + cnt == a1);
+        // advance
+        piece_start = false;
+        key += cnt;
+        pos += cnt;
+        if (key == Lb && pos < a1) {
+            key = 0;
+            piece_start = true;
+            if (++sub == nsub) {
+                sub = 0;
+                do {  // next non-empty sequence (one exists: pos < a1)
+                    ++b;
+                    if (++f == 64) {
+                        f = 0;
+                        pb += 64;
+                        pageL = pb + lane < B ? clamp_len(seq_lens[pb + lane], Lmax) : 0;
+                    }
+                    Lb = __builtin_amdgcn_readlane(pageL, f);
+                } while (Lb == 0 && b + 1 < B);
             }
         }
+        return true;
+    };
+
+    // ---- operand read offsets (bytes), fixed for the kernel --------------
+    const int n = lane & 15, g = lane >> 4;
+    // K (A operand, m = key n of a 16-key half) and Q (B operand, n = head):
+    // row n, chunk 4 kk + g; a half-chunk t adds 16 rows (same swizzle).
+    int k_off[C::KS], q_off[C::KS];
+    const int qn = n & (S::QROWS - 1);  // Q slot row read by this lane (lanes past QROWS get zeros)
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const bool valid = base + u * KW + sub < k_end;
-            float vf[8];
+    for (int kk = 0; kk < C::KS; ++kk) {
+        k_off[kk] = n * D * 2 + (((4 * kk + g) ^ swz_k<D>(n)) * 16);
+        q_off[kk] = qn * D * 2 + (((4 * kk + g) ^ swz_k<D>(qn)) * 16);
+    }
+    // V (transposing reads): a 16-lane group g reads keys 4g .. 4g+3 (+16 for
+    // the second half) x 16 columns of block cb; this lane's 8 bytes are key
+    // 4g + (n >> 2), columns 16 cb + 4 (n & 3) .. + 3.
+    int v_off[C::CB];
+    {
+        const int row = 4 * g + (n >> 2);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                vf[2 * i] = __builtin_bit_cast(float, vr[u][i] << 16);
-                vf[2 * i + 1] = __builtin_bit_cast(float, vr[u][i] & 0xffff0000u);
-            }
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
-                const float dsum = row_sum<CH>(dot8(qv[hh], kr[u]));
-                const float sc = valid ? dsum * sl2 : -INFINITY;
-                if (sc > m[hh] + RESCALE_TH) {  // raise the reference (rare)
-                    const float alpha = __builtin_amdgcn_exp2f(m[hh] - sc);
-                    l[hh] *= alpha;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[hh][e] *= alpha;
-                    m[hh] = sc;
-                }
-                const float p = valid ? __builtin_amdgcn_exp2f(sc - m[hh]) : 0.f;
-                l[hh] += p;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(p, vf[e], acc[hh][e]);
-            }
+        for (int cb = 0; cb < C::CB; ++cb) {
+            const int col = 16 * cb + 4 * (n & 3);
+            v_off[cb] = row * D * 2 + ((((col >> 3) ^ swz_v<D>(row))) * 16) + (col & 7) * 2;
         }
     }
 
-    // merge the KW lane groups of this wave (they hold different rows)
+    // ---- running state of the current piece ------------------------------
+    f32x4 acc[C::CB];
 #pragma unroll
-    for (int x = CH; x < 64; x <<= 1) {
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            const float mp = __shfl_xor(m[hh], x, 64);
-            const float lp = __shfl_xor(l[hh], x, 64);
-            const float M = fmaxf(m[hh], mp);
-            const float Mu = (M == -INFINITY) ? 0.f : M;
-            const float f = __builtin_amdgcn_exp2f(m[hh] - Mu);
-            const float fp = __builtin_amdgcn_exp2f(mp - Mu);
-            l[hh] = l[hh] * f + lp * fp;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float ap = __shfl_xor(acc[hh][e], x, 64);
-                acc[hh][e] = acc[hh][e] * f + ap * fp;
-            }
-            m[hh] = M;
-        }
-    }
-    if (sub == 0) {
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s_acc[wave][hh][ch * 8 + e] = acc[hh][e];
-            if (ch == 0) {
-                s_m[wave][hh] = m[hh];
-                s_l[wave][hh] = l[hh];
-            }
-        }
-    }
-    __syncthreads();
+    for (int cb = 0; cb < C::CB; ++cb) acc[cb] = f32x4{};
+    float m_ref = 0.f, l_run = 0.f;
 
-    // merge the waves and write this split's partial result
-    for (int idx = tid; idx < G * D; idx += NTHR) {
-        const int hh = idx / D, c = idx % D;
-        float M = -INFINITY;
+    auto compute = [&](const int st) {
+        const char *src = lds + st * S::BYTES;
+        const int cnt = m_cnt[st];
+        // operands
+        bf16x8 qb[C::KS];
 #pragma unroll
-        for (int w = 0; w < NWAVE; ++w) M = fmaxf(M, s_m[w][hh]);
-        const float Mu = (M == -INFINITY) ? 0.f : M;
-        float lt = 0.f, ot = 0.f;
-#pragma unroll
-        for (int w = 0; w < NWAVE; ++w) {
-            const float f = __builtin_amdgcn_exp2f(s_m[w][hh] - Mu);
-            lt += s_l[w][hh] * f;
-            ot += s_acc[w][hh][c] * f;
+        for (int kk = 0; kk < C::KS; ++kk) {
+            u32x4 x = *reinterpret_cast<const u32x4 *>(src + S::Q_OFF + q_off[kk]);
+            if (neg) x ^= 0x80008000u;
+            if (S::QROWS < 16 && n >= S::QROWS) x = u32x4{};  // heads beyond the stored rows
+            qb[kk] = __builtin_bit_cast(bf16x8, x);
         }
-        const size_t row = (size_t)(b * Hq + hk * G + hh) * n_splits + split;
-        ws_o[row * D + c] = ot / lt;  // lt > 0: the split holds at least one valid row
-        if (c == 0) ws_lse[row] = (Mu + __log2f(lt)) * LN2;
+        bf16x8 ka[2][C::KS];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int kk = 0; kk < C::KS; ++kk)
+                ka[t][kk] = *reinterpret_cast<const bf16x8 *>(src + S::K_OFF + t * 16 * D * 2 + k_off[kk]);
+        bf16x8 va[C::CB];
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb) {
+            i16x4 part[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4 *)(src + S::V_OFF + h * 16 * D * 2 + v_off[cb]));
+            va[cb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+        // scores: lane holds head n, keys 16 t + 4 g + r
+        f32x4 s[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+        for (int kk = 0; kk < C::KS; ++kk)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t][kk], qb[kk], s[t], 0, 0, 0);
+        float x[8];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[4 * t + r] = s[t][r];
+        if (cnt < CK) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (16 * (i >> 2) + 4 * g + (i & 3) >= cnt) x[i] = -INFINITY;
+        }
+        auto head_max = [&]() {
+            float mx = x[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            return mx * sl2;  // finite: key 0 of the chunk is valid
+        };
+        if (m_first[st]) {
+            m_ref = head_max();
+            l_run = 0.f;
+#pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb) acc[cb] = f32x4{};
+        }
+        float p[8], psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            p[i] = __builtin_amdgcn_exp2f(fmaf(x[i], sl2, -m_ref));
+            psum += p[i];
+        }
+        if (__builtin_amdgcn_ballot_w64(!(psum <= RESCALE_SUM)) != 0) {
+            // raise the reference to the running max (rare)
+            const float m_new = fmaxf(m_ref, head_max());
+            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb) acc[cb] *= alpha;
+            m_ref = m_new;
+            psum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                p[i] = __builtin_amdgcn_exp2f(fmaf(x[i], sl2, -m_ref));
+                psum += p[i];
+            }
+        }
+        l_run += psum;
+        const u32x4 pw = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
+                          pack_bf16(p[6], p[7])};
+        const bf16x8 pbv = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb) acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[cb], pbv, acc[cb], 0, 0, 0);
+
+        if (m_last[st]) {
+            // end of this range's piece of the segment: normalised partial
+            // output and log-sum-exp go to slot (segment + workgroup)
+            float lt = l_run + __shfl_xor(l_run, 16, 64);
+            lt += __shfl_xor(lt, 32, 64);
+            const size_t slot = (size_t)m_seg[st] + w;
+            if (n < m_gblk[st]) {
+                const float inv = 1.f / lt;
+                float *dst = ws_o + (slot * GB + n) * D + 4 * g;
+#pragma unroll
+                for (int cb = 0; cb < C::CB; ++cb) *reinterpret_cast<f32x4 *>(dst + 16 * cb) = acc[cb] * inv;
+                if (g == 0) ws_lse[slot * GB + n] = (m_ref + __log2f(lt)) * LN2;
+            }
+        }
+    };
+
+    // ---- the pipeline ------------------------------------------------------
+    int issued = 0, done = 0;
+#pragma unroll
+    for (int u = 0; u < NST - 1; ++u)
+        if (issue(u)) ++issued;
+    // one pipeline step on stage u (a constant after inlining); false once
+    // every issued chunk has been computed
+    auto step = [&](const int u) {
+        if (done == issued) return false;
+        // chunk `done` sits in stage u; `after` chunks were issued after it
+        const int after = issued - done - 1;
+        if (after >= NST - 2) {
+            wait_vmcnt<(NST - 2) * S::NI>();
+        } else if (NST > 3 && after == 1) {
+            wait_vmcnt<S::NI>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        // the stage refilled next was consumed by the previous chunk
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (issue((u + NST - 1) % NST)) ++issued;
+        compute(u);
+        ++done;
+        return true;
+    };
+    for (;;) {
+        if (!step(0)) return;
+        if (!step(1)) return;
+        if constexpr (NST > 2) {
+            if (!step(2)) return;
+        }
+        if constexpr (NST > 3) {
+            if (!step(3)) return;
+        }
     }
 }
 
+// Combines the partial results of each segment: lse = ln sum_w exp(lse_w),
+// o = sum_w exp(lse_w - lse) o_w, over the workgroups w whose ranges touch the
+// segment.  One workgroup per segment.
 template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(
+__global__ __launch_bounds__(256) void decode_merge_kernel(
     const float *__restrict__ ws_o, const float *__restrict__ ws_lse, const int32_t *__restrict__ seq_lens,
-    __bf16 *__restrict__ O, float *__restrict__ LSE, int Hq, int Lmax, int kps, int n_splits)
+    __bf16 *__restrict__ O, float *__restrict__ LSE, int B, int Hq, int Hkv, int Lmax, int nhb, int n_wg)
 {
-    const int bh = blockIdx.x;
-    const int b = bh / Hq;
-    const int c = threadIdx.x;
-    int L = seq_lens[b];
-    L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
-    const int ns = (L + kps - 1) / kps;
-    const float *lse_s = ws_lse + (size_t)bh * n_splits;
-    const float *o_s = ws_o + (size_t)bh * n_splits * D;
-    float lse = -INFINITY, o = 0.f;
-    if (ns > 0) {
-        float M = -INFINITY;
-        for (int s = 0; s < ns; ++s) M = fmaxf(M, lse_s[s]);
-        float S = 0.f;
-        for (int s = 0; s < ns; ++s) S += expf(lse_s[s] - M);
-        lse = M + logf(S);
-        for (int s = 0; s < ns; ++s) o = fmaf(expf(lse_s[s] - lse), o_s[(size_t)s * D + c], o);
+    const int seg = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int G = Hq / Hkv;
+    const int GB = G < 16 ? G : 16;
+    const int nsub = Hkv * nhb;
+    const int b = seg / nsub, sub = seg - b * nsub;
+    const int hk = sub / nhb, hb = sub - hk * nhb;
+    const int gblk = G - 16 * hb < 16 ? G - 16 * hb : 16;
+    const size_t head0 = (size_t)b * Hq + hk * G + 16 * hb;
+
+    // prefix of the segment and the batch total (every wave computes them)
+    long long T = 0, Pb = 0;
+    for (int pb = 0; pb < B; pb += 64) {
+        const int L = pb + lane < B ? clamp_len(seq_lens[pb + lane], Lmax) : 0;
+        const int s = wave_incl_scan(L, lane);
+        if (b >= pb && b < pb + 64) Pb = T + __builtin_amdgcn_readlane(s, b - pb) - __builtin_amdgcn_readlane(L, b - pb);
+        T += __builtin_amdgcn_readlane(s, 63);
     }
-    O[(size_t)bh * D + c] = (__bf16)o;
-    if (LSE && c == 0) LSE[bh] = lse;
+    T *= nsub;
+    const int Lb = clamp_len(seq_lens[b], Lmax);
+    constexpr int C4 = D / 4;
+    if (Lb == 0) {  // no visible key: O = 0, LSE = -inf
+        for (int idx = tid; idx < gblk * C4; idx += 256) {
+            const int h = idx / C4, c4 = idx - h * C4;
+            *reinterpret_cast<bf16x4 *>(O + (head0 + h) * D + 4 * c4) = bf16x4{};
+            if (c4 == 0 && LSE) LSE[head0 + h] = -INFINITY;
+        }
+        return;
+    }
+    const long long S0 = Pb * nsub + (long long)sub * Lb, S1 = S0 + Lb;
+    const int w0 = (int)(((S0 + 1) * n_wg - 1) / T);
+    const int w1 = (int)((S1 * n_wg - 1) / T);
+    for (int idx = tid; idx < gblk * C4; idx += 256) {
+        const int h = idx / C4, c4 = idx - h * C4;
+        // one pass with a running maximum; workgroups with empty ranges
+        // wrote nothing and are skipped
+        float M = -INFINITY, sum = 0.f;
+        f32x4 o = f32x4{};
+        long long lo = range_start(w0, T, n_wg);
+        for (int wg = w0; wg <= w1; ++wg) {
+            const long long hi = range_start(wg + 1, T, n_wg);
+            if (lo < hi) {
+                const size_t slot = (size_t)seg + wg;
+                const float l = ws_lse[slot * GB + h];
+                const f32x4 ov = *reinterpret_cast<const f32x4 *>(ws_o + (slot * GB + h) * D + 4 * c4);
+                if (l > M) {
+                    const float r = __expf(M - l);
+                    sum *= r;
+                    o *= r;
+                    M = l;
+                }
+                const float e = __expf(l - M);
+                sum += e;
+                o += e * ov;
+            }
+            lo = hi;
+        }
+        o *= 1.f / sum;
+        *reinterpret_cast<bf16x4 *>(O + (head0 + h) * D + 4 * c4) = __builtin_convertvector(o, bf16x4);
+        if (c4 == 0 && LSE) LSE[head0 + h] = M + __logf(sum);
+    }
 }
 
-template <int D, int G>
-hipError_t launch_g(const DecodeArgs &a, hipStream_t stream) {
+template <int D, int QR, int NST>
+hipError_t launch_cfg(const DecodeArgs &a, hipStream_t stream) {
+    using S = Stage<D, QR>;
+    const size_t lds_bytes = (size_t)NST * S::BYTES;
+    int n_wg = a.n_wg;
+    if (n_wg <= 0) {
+        // as many single-wave workgroups as the chip holds at once
+        static int cached[64];
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+        if (cached[dev] == 0) {
+            int cus = 0, per_cu = 0;
+            hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+            if (e != hipSuccess) return e;
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_chunk_kernel<D, QR, NST>, 64,
+                                                             lds_bytes);
+            if (e != hipSuccess) return e;
+            cached[dev] = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+        }
+        n_wg = cached[dev];
+    }
+    if (n_wg > a.max_wg) n_wg = a.max_wg;
     const float sl2 = a.scale * LOG2E;
-    hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(a.n_splits, a.Hkv, a.B), dim3(NTHR), 0, stream,
-                       (const __bf16 *)a.q, (const __bf16 *)a.k_cache, (const __bf16 *)a.v_cache, a.seq_lens,
-                       a.ws_o, a.ws_lse, a.Hq, a.Hkv, a.Lmax, a.keys_per_split, a.n_splits, sl2);
+    hipLaunchKernelGGL((decode_chunk_kernel<D, QR, NST>), dim3(n_wg), dim3(64), lds_bytes, stream,
+                       (const __bf16 *)a.q, (const __bf16 *)a.k_cache, (const __bf16 *)a.v_cache, a.seq_lens, a.ws_o,
+                       a.ws_lse, a.B, a.Hq, a.Hkv, a.Lmax, a.nhb, n_wg, sl2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.B * a.Hq), dim3(D), 0, stream, a.ws_o, a.ws_lse,
-                       a.seq_lens, (__bf16 *)a.o, a.lse, a.Hq, a.Lmax, a.keys_per_split, a.n_splits);
+    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.B * a.Hkv * a.nhb), dim3(256), 0, stream, a.ws_o, a.ws_lse,
+                       a.seq_lens, (__bf16 *)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Lmax, a.nhb, n_wg);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const DecodeArgs &a, hipStream_t stream) {
-    switch (a.Hq / a.Hkv) {
-        case 1: return launch_g<D, 1>(a, stream);
-        case 2: return launch_g<D, 2>(a, stream);
-        case 4: return launch_g<D, 4>(a, stream);
-        case 8: return launch_g<D, 8>(a, stream);
-        case 16: return launch_g<D, 16>(a, stream);
-        default: return hipErrorInvalidValue;
-    }
+    const int G = a.Hq / a.Hkv;
+    return G <= 4 ? launch_cfg<D, 4, DECODE_STAGES>(a, stream) : launch_cfg<D, 16, DECODE_STAGES>(a, stream);
 }
 
 }  // namespace

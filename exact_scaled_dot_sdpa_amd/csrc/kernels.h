@@ -23,10 +23,11 @@ struct DecodeArgs {
     float *lse;
     int B, Hq, Hkv, Lmax, d;
     float scale;
-    int keys_per_split;
-    int n_splits;
-    float *ws_o;    // [B, Hq, n_splits, d] fp32
-    float *ws_lse;  // [B, Hq, n_splits] fp32
+    int nhb;        // blocks of up to 16 query heads per K/V head: ceil(G / 16)
+    int n_wg;       // workgroups of the split kernel; 0 = as many as the device holds at once
+    int max_wg;     // workgroups the workspace has partial-result slots for
+    float *ws_o;    // [B*Hkv*nhb + max_wg - 1 slots, min(G, 16) heads, d] fp32
+    float *ws_lse;  // [slots, min(G, 16)] fp32
 };
 
 // Each returns hipSuccess or the launch error.

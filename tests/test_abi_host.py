@@ -79,13 +79,9 @@ def dec(q=P, kc=P, vc=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Lmax=512, d=128, sc
     (dict(B=-1), E.ATTN_ERR_INVALID_ARG),
     (dict(Lmax=-1), E.ATTN_ERR_INVALID_ARG),
     (dict(scale=float("nan")), E.ATTN_ERR_INVALID_ARG),
-    (dict(kps=100), E.ATTN_ERR_INVALID_ARG),            # not a multiple of 64
-    (dict(kps=32), E.ATTN_ERR_INVALID_ARG),
-    (dict(kps=1 << 17), E.ATTN_ERR_INVALID_ARG),
+    (dict(kps=-1), E.ATTN_ERR_INVALID_ARG),
     (dict(dtype=0), E.ATTN_ERR_UNSUPPORTED),            # fp32 decode not implemented
     (dict(d=96), E.ATTN_ERR_UNSUPPORTED),
-    (dict(Hq=6, Hkv=2), E.ATTN_ERR_UNSUPPORTED),        # group of 3
-    (dict(Hq=64, Hkv=2), E.ATTN_ERR_UNSUPPORTED),       # group of 32
     (dict(sl=None), E.ATTN_ERR_INVALID_ARG),
     (dict(sl=P + 2), E.ATTN_ERR_INVALID_ARG),
     (dict(q=None), E.ATTN_ERR_INVALID_ARG),
@@ -99,16 +95,32 @@ def test_decode_validation(kw, status):
     assert dec(**kw) == status
 
 
+def _ws_bytes(B, Hq, Hkv, Lmax, d, kps):
+    """The workspace size the header documents: slots of min(G, 16) heads,
+    one per (sequence, K/V head, block of 16 query heads) plus one per split
+    workgroup beyond the first; fp32 outputs (256-byte aligned), then fp32
+    LSEs."""
+    G = Hq // Hkv
+    nhb = -(-G // 16)
+    gb = min(G, 16)
+    if kps > 0:
+        n_wg = min(max(-(-(B * Hkv * nhb * Lmax) // kps), 1), 2048)
+    else:
+        n_wg = 2048
+    rows = (B * Hkv * nhb + n_wg - 1) * gb
+    return -(-(rows * d * 4) // 256) * 256 + rows * 4
+
+
 def test_decode_workspace_bytes():
     f = E.attn_decode_workspace_bytes
-    # default split of 256 keys: S = ceil(4096 / 256) = 16
-    rows = 16 * 32 * 16
-    assert f(16, 32, 8, 4096, 128) == ((rows * 128 * 4 + 255) // 256) * 256 + rows * 4
-    assert f(16, 32, 8, 4096, 128, 1024) == 16 * 32 * 4 * 128 * 4 + 16 * 32 * 4 * 4
-    assert f(1, 1, 1, 0, 64) == 256 + 4            # at least one split
+    for args in [(16, 32, 8, 4096, 128, 0), (16, 32, 8, 4096, 128, 1024), (1, 1, 1, 0, 64, 0),
+                 (3, 6, 2, 100, 64, 0), (2, 64, 2, 777, 128, 100), (2, 40, 2, 300, 64, 7)]:
+        assert f(*args) == _ws_bytes(*args), args
+    # 16 x 8 segments + 512 workgroups of 1024 keys - 1, four heads each
+    assert f(16, 32, 8, 4096, 128, 1024) == 639 * 4 * 128 * 4 + 639 * 4 * 4
     assert f(1, 3, 2, 100, 64) == 0                  # invalid sizes
     assert f(1, 2, 1, 100, 96) == 0
-    assert f(1, 2, 1, 100, 64, 100) == 0
+    assert f(1, 2, 1, 100, 64, -1) == 0
     # exactly the workspace that size reports is accepted, one byte less is not
     need = f(2, 8, 2, 512, 128)
     assert dec(ws_bytes=need - 1) == E.ATTN_ERR_WORKSPACE

@@ -1,4 +1,11 @@
-"""Parity of attn_decode (the split-KV HIP kernels) with the fp64 oracle."""
+"""Parity of attn_decode (the split-KV HIP kernels) with the fp64 oracle.
+
+The split kernel cuts the keys of the whole batch (every sequence, K/V head
+and block of 16 query heads laid end to end) into equal ranges, one per
+workgroup; keys_per_split sets the range length (0: one range per workgroup
+the device holds at once).  The cases below cover ranges shorter than a
+chunk, ranges that span many short sequences, several pages of 64 sequences,
+empty sequences and workgroups whose range is empty."""
 import numpy as np
 import pytest
 import torch
@@ -27,7 +34,7 @@ def test_c5_full_parity(orc):
     _parity(orc, sl, q, kc, vc, w.scale, "C5")
 
 
-@pytest.mark.parametrize("kps", [64, 128, 512, 4096])
+@pytest.mark.parametrize("kps", [1, 64, 100, 512, 4096, 1 << 20])
 def test_split_count_invariance(orc, kps):
     sl, q, kc, vc = I.decode_inputs(4, 32, 8, 2048, 128, "bf16", seed=61, lo=1, hi=2048)
     o_ref, l_ref = gpu_decode(sl, q, kc, vc, 0.088, 0)
@@ -36,7 +43,8 @@ def test_split_count_invariance(orc, kps):
     assert_close("kps=%d vs default (O)" % kps, o, o_ref, 2 ** -6)
 
 
-@pytest.mark.parametrize("G,d", [(1, 128), (2, 64), (4, 64), (8, 128), (16, 128), (16, 64)])
+@pytest.mark.parametrize("G,d", [(1, 128), (2, 64), (3, 128), (4, 64), (5, 64), (8, 128), (16, 128), (16, 64),
+                                 (24, 128), (32, 64)])
 def test_group_sizes(orc, G, d):
     Hkv = 2
     sl, q, kc, vc = I.decode_inputs(3, G * Hkv, Hkv, 700, d, "bf16", seed=70 + G, lo=1, hi=700)
@@ -54,6 +62,32 @@ def test_edge_lengths(orc):
     o_ref, l_ref = orc.decode(I.to_f64(q), I.to_f64(kc), I.to_f64(vc), sl.numpy(), 0.088)
     assert_close("edge lengths O", o, o_ref, TOL_O["bf16"])
     assert_close("edge lengths LSE", lse, l_ref, TOL_LSE)
+    # one key per workgroup range: most of the 2048 workgroups get no key
+    o, lse = gpu_decode(sl, q, kc, vc, 0.088, keys_per_split=1)
+    assert_close("edge lengths O, 1-key ranges", o, o_ref, TOL_O["bf16"])
+    assert_close("edge lengths LSE, 1-key ranges", lse, l_ref, TOL_LSE)
+
+
+@pytest.mark.parametrize("kps", [0, 1, 33])
+def test_many_short_sequences(orc, kps):
+    """150 sequences (three pages of 64) of 0..40 keys, some empty: ranges
+    cross many sequence boundaries and several workgroups get no keys."""
+    B, Hq, Hkv, Lmax, d = 150, 8, 2, 48, 128
+    _, q, kc, vc = I.decode_inputs(B, Hq, Hkv, Lmax, d, "bf16", seed=85)
+    g = torch.Generator().manual_seed(86)
+    sl = torch.randint(0, 41, (B,), generator=g, dtype=torch.int32)
+    sl[::7] = 0
+    o, lse = _parity(orc, sl, q, kc, vc, 0.088, "150 short sequences", kps)
+    assert (o[sl.numpy() == 0] == 0).all() and np.isneginf(lse[sl.numpy() == 0]).all()
+
+
+def test_empty_cache():
+    """max_seq_len = 0: every row sees no key."""
+    B, Hq, Hkv, d = 3, 8, 2, 64
+    q = torch.randn(B, Hq, d).to(torch.bfloat16)
+    kc = torch.empty(B, Hkv, 0, d, dtype=torch.bfloat16)
+    o, lse = gpu_decode(torch.zeros(B, dtype=torch.int32), q, kc, kc.clone(), 0.125)
+    assert (o == 0).all() and np.isneginf(lse).all()
 
 
 def test_nan_padding_never_read():
