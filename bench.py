@@ -237,7 +237,7 @@ def main():
         out["roofline_decode"] = {
             "bound": "hbm", "achieved": round(d_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(d_gbs / PEAK_HBM_GBS, 4), "traffic": tr,
-            "kernel": "decode_split_kernel<128,4> + decode_merge_kernel<128>", "avg_launch_ms": round(d_ms, 5),
+            "kernel": "decode_chunk_kernel<128,4,3> + decode_merge_kernel<128>", "avg_launch_ms": round(d_ms, 5),
         }
     if not args.no_cpu_baseline and run_p:
         out["cpu_baseline"] = cpu_baseline(q_cpu, k_cpu, v_cpu, wp, args.cpu_seconds)

@@ -14,12 +14,14 @@
 // into n_wg equal ranges, one per single-wave workgroup.  With n_wg set to the
 // number of workgroups the chip holds at once, every workgroup streams the
 // same number of bytes whatever the length mix of the batch.  A range that
-// covers part of a segment produces a partial result (normalised output and
-// log-sum-exp of its keys); the merge kernel combines the partials of each
-// segment, which is one more step of the online-softmax recurrence
-// ("从注意力到 IO 感知执行", sec. 8, eqs. (1)-(2)) applied to whole ranges.
-// Every workgroup computes the segment prefix sums itself from seq_lens (a
-// 64-lane scan per 64 sequences); no planning kernel runs first.
+// covers a whole segment writes its output rows directly.  A range that
+// covers part of a segment writes a partial result (normalised output and
+// log-sum-exp of its keys) to the workspace; a second kernel merges the
+// partials of each shared segment, which is one more step of the
+// online-softmax recurrence ("从注意力到 IO 感知执行", sec. 8, eqs. (1)-(2))
+// applied to whole ranges.  Every workgroup computes the segment prefix sums
+// itself from seq_lens (a 64-lane scan per 64 sequences); no planning kernel
+// runs first.
 //
 // gfx950 mapping inside a workgroup (one wave):
 //   * The range is walked in chunks of 32 keys (fewer at the end of a segment
@@ -131,18 +133,6 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Sum over the keys of the whole batch, in units of keys x segments:
-// T = nsub * sum_b clamp(seq_lens[b]).  Wave-uniform.
-__device__ __forceinline__ long long total_keys(const int32_t *seq_lens, int B, int Lmax, int nsub, int lane) {
-    long long t = 0;
-    for (int pb = 0; pb < B; pb += 64) {
-        const int L = pb + lane < B ? clamp_len(seq_lens[pb + lane], Lmax) : 0;
-        const int s = wave_incl_scan(L, lane);
-        t += __builtin_amdgcn_readlane(s, 63);
-    }
-    return t * nsub;
-}
-
 // First key position of workgroup w's range: floor(w * T / n_wg).
 __device__ __forceinline__ long long range_start(long long w, long long T, int n_wg) { return w * T / n_wg; }
 
@@ -173,11 +163,85 @@ __device__ __forceinline__ void dma_chunk(char *dst, const __bf16 *k, const __bf
                                                  i * 1024, 0, 0);
 }
 
+// Merge of one segment's partial results (one wave): lse = ln sum_w
+// exp(lse_w), o = sum_w exp(lse_w - lse) o_w over the workgroups w0..w1 with
+// a non-empty range, i.e. one more step of the online-softmax recurrence
+// applied to whole key ranges.  Writes the gblk output rows from head0.
+template <int D>
+__device__ void merge_segment(const float *ws_o, const float *ws_lse, __bf16 *O, float *LSE, int seg, int w0, int w1,
+                              size_t head0, int gblk, int GB, long long T, int n_wg, int lane) {
+    constexpr int C4 = D / 4;  // float4 groups per output row
+    constexpr int RO = 2;      // outputs (float4) per lane per round
+    constexpr int PB = 6;      // pieces whose loads are in flight together
+    const int nout = gblk * C4;
+    for (int base = 0; base < nout; base += 64 * RO) {
+        int h[RO], c4[RO];
+        bool act[RO];
+        float M[RO], sum[RO];
+        f32x4 o[RO];
+#pragma unroll
+        for (int r = 0; r < RO; ++r) {
+            const int idx = base + 64 * r + lane;
+            act[r] = idx < nout;
+            h[r] = act[r] ? idx / C4 : 0;
+            c4[r] = act[r] ? idx - h[r] * C4 : 0;
+            M[r] = -INFINITY;
+            sum[r] = 0.f;
+            o[r] = f32x4{};
+        }
+        for (int wb = w0; wb <= w1; wb += PB) {
+            float l[PB][RO];
+            f32x4 ov[PB][RO];
+#pragma unroll
+            for (int j = 0; j < PB; ++j) {
+                const int wg = wb + j;
+                const bool ok = wg <= w1 && (T >= n_wg || range_start(wg, T, n_wg) < range_start(wg + 1, T, n_wg));
+#pragma unroll
+                for (int r = 0; r < RO; ++r) {
+                    l[j][r] = -INFINITY;
+                    ov[j][r] = f32x4{};
+                }
+                if (ok) {  // uniform
+                    const size_t slot = (size_t)seg + wg;
+#pragma unroll
+                    for (int r = 0; r < RO; ++r) {
+                        l[j][r] = ws_lse[slot * GB + h[r]];
+                        ov[j][r] = *reinterpret_cast<const f32x4 *>(ws_o + (slot * GB + h[r]) * D + 4 * c4[r]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < PB; ++j) {
+#pragma unroll
+                for (int r = 0; r < RO; ++r) {
+                    if (l[j][r] == -INFINITY) continue;  // absent piece (a present one has a finite lse)
+                    if (l[j][r] > M[r]) {
+                        const float sc = __expf(M[r] - l[j][r]);
+                        sum[r] *= sc;
+                        o[r] *= sc;
+                        M[r] = l[j][r];
+                    }
+                    const float e = __expf(l[j][r] - M[r]);
+                    sum[r] += e;
+                    o[r] += e * ov[j][r];
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RO; ++r) {
+            if (!act[r]) continue;
+            const f32x4 res = o[r] * (1.f / sum[r]);
+            *reinterpret_cast<bf16x4 *>(O + (head0 + h[r]) * D + 4 * c4[r]) = __builtin_convertvector(res, bf16x4);
+            if (LSE && c4[r] == 0) LSE[head0 + h[r]] = M[r] + __logf(sum[r]);
+        }
+    }
+}
+
 template <int D, int QR, int NST>
 __global__ __launch_bounds__(64) void decode_chunk_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ Kc, const __bf16 *__restrict__ Vc,
-    const int32_t *__restrict__ seq_lens, float *__restrict__ ws_o, float *__restrict__ ws_lse, int B, int Hq,
-    int Hkv, int Lmax, int nhb, int n_wg, float sl2)
+    const int32_t *__restrict__ seq_lens, __bf16 *__restrict__ O, float *__restrict__ LSE, float *__restrict__ ws_o,
+    float *__restrict__ ws_lse, int B, int Hq, int Hkv, int Lmax, int nhb, int n_wg, float sl2)
 {
     using C = DC<D>;
     using S = Stage<D, QR>;
@@ -190,16 +254,35 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
     const int nsub = Hkv * nhb;      // segments per sequence
 
     // ---- this workgroup's key range [a0, a1) -----------------------------
-    const long long T = total_keys(seq_lens, B, Lmax, nsub, lane);
+    // The first page of 64 sequence lengths serves both the total and the
+    // search, so a batch of up to 64 sequences costs one memory round trip.
+    int pageL = lane < B ? clamp_len(seq_lens[lane], Lmax) : 0;
+    int incl = wave_incl_scan(pageL, lane);
+    long long T = __builtin_amdgcn_readlane(incl, 63);
+    for (int p2 = 64; p2 < B; p2 += 64) {
+        const int L = p2 + lane < B ? clamp_len(seq_lens[p2 + lane], Lmax) : 0;
+        T += __builtin_amdgcn_readlane(wave_incl_scan(L, lane), 63);
+    }
+    T *= nsub;
+    // sequences with no visible key (seq_len 0) get O = 0 and LSE = -inf from
+    // workgroup b mod n_wg; no range ever reaches them
+    for (int bz = w; bz < B; bz += n_wg) {
+        const int L = bz < 64 ? __builtin_amdgcn_readlane(pageL, bz) : clamp_len(seq_lens[bz], Lmax);
+        if (L == 0) {
+            __bf16 *dst = O + (size_t)bz * Hq * D;
+            for (int i = lane; i < Hq * D / 8; i += 64) *reinterpret_cast<u32x4 *>(dst + 8 * i) = u32x4{};
+            if (LSE)
+                for (int i = lane; i < Hq; i += 64) LSE[(size_t)bz * Hq + i] = -INFINITY;
+        }
+    }
     const long long a0 = range_start(w, T, n_wg), a1 = range_start(w + 1, T, n_wg);
     if (a0 >= a1) return;
 
-    // locate a0: sequence b (page pb, lane f), segment sub, key
-    int pb = 0, f = 0, pageL = 0;
+    // locate a0: sequence b (page pb, lane f), segment sub, key; bstart is the
+    // position of sequence b's first key in the batch list
+    int pb = 0, f = 0;
     long long bstart = 0;
-    for (;; pb += 64) {  // a0 < T, so some page holds it
-        pageL = pb + lane < B ? clamp_len(seq_lens[pb + lane], Lmax) : 0;
-        const int incl = wave_incl_scan(pageL, lane);
+    for (;;) {  // a0 < T, so some page holds it
         const long long end_i = bstart + (long long)incl * nsub;
         const unsigned long long hit = __builtin_amdgcn_ballot_w64(end_i > a0);
         if (hit) {
@@ -208,6 +291,9 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
             break;
         }
         bstart += (long long)__builtin_amdgcn_readlane(incl, 63) * nsub;
+        pb += 64;
+        pageL = pb + lane < B ? clamp_len(seq_lens[pb + lane], Lmax) : 0;
+        incl = wave_incl_scan(pageL, lane);
     }
     int b = pb + f;
     int Lb = __builtin_amdgcn_readlane(pageL, f);
@@ -235,9 +321,12 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
         voff_v[i] = ld_q * D * 2 + ((ld_p ^ swz_v<D>(R)) * 16);
     }
 
-    // per-stage chunk records (wave-uniform)
-    int m_seg[NST], m_cnt[NST], m_gblk[NST];
+    // per-stage chunk records (wave-uniform): segment, key count, heads,
+    // first / last chunk of this range's piece of the segment, the first and
+    // last workgroup whose range touches the segment, first output row
+    int m_seg[NST], m_cnt[NST], m_gblk[NST], m_w0[NST], m_w1[NST], m_head0[NST];
     bool m_first[NST], m_last[NST];
+    int cur_w0 = 0, cur_w1 = 0;  // of the segment the cursor is in
 
     // Issue the loads of the next chunk of the range into stage st and
     // advance the cursor; false (nothing issued) once the range is done.
@@ -253,12 +342,20 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
         }
         const int hk = sub / nhb, hb = sub - hk * nhb;
         const int gblk = G - 16 * hb < 16 ? G - 16 * hb : 16;
+        if (piece_start) {
+            const long long S0 = bstart + (long long)sub * Lb, S1 = S0 + Lb;
+            cur_w0 = (int)(((S0 + 1) * n_wg - 1) / T);
+            cur_w1 = (int)((S1 * n_wg - 1) / T);
+        }
         const size_t row0 = (size_t)(b * Hkv + hk) * Lmax + key;
         dma_chunk<D, QR>(lds + st * S::BYTES, Kc + row0 * D, Vc + row0 * D,
                          Q + ((size_t)b * Hq + hk * G + 16 * hb) * D, cnt * D * 2, gblk * D * 2, voff_k, voff_v);
         m_seg[st] = b * nsub + sub;
         m_cnt[st] = cnt;
         m_gblk[st] = gblk;
+        m_w0[st] = cur_w0;
+        m_w1[st] = cur_w1;
+        m_head0[st] = b * Hq + hk * G + 16 * hb;
         m_first[st] = piece_start;
         m_last[st] = (key + cnt == Lb) || (pos + cnt == a1);
         // advance
@@ -271,6 +368,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
             if (++sub == nsub) {
                 sub = 0;
                 do {  // next non-empty sequence (one exists: pos < a1)
+                    bstart += (long long)Lb * nsub;
                     ++b;
                     if (++f == 64) {
                         f = 0;
@@ -401,17 +499,31 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
         for (int cb = 0; cb < C::CB; ++cb) acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[cb], pbv, acc[cb], 0, 0, 0);
 
         if (m_last[st]) {
-            // end of this range's piece of the segment: normalised partial
-            // output and log-sum-exp go to slot (segment + workgroup)
+            // end of this range's piece of the segment
             float lt = l_run + __shfl_xor(l_run, 16, 64);
             lt += __shfl_xor(lt, 32, 64);
-            const size_t slot = (size_t)m_seg[st] + w;
-            if (n < m_gblk[st]) {
-                const float inv = 1.f / lt;
-                float *dst = ws_o + (slot * GB + n) * D + 4 * g;
+            const int gblk = m_gblk[st], seg = m_seg[st];
+            const float inv = 1.f / lt;
+            const float lse_piece = (m_ref + __log2f(lt)) * LN2;
+            if (m_w0[st] == m_w1[st]) {
+                // the whole segment lies in this range: the final result
+                if (n < gblk) {
+                    __bf16 *dst = O + ((size_t)m_head0[st] + n) * D + 4 * g;
 #pragma unroll
-                for (int cb = 0; cb < C::CB; ++cb) *reinterpret_cast<f32x4 *>(dst + 16 * cb) = acc[cb] * inv;
-                if (g == 0) ws_lse[slot * GB + n] = (m_ref + __log2f(lt)) * LN2;
+                    for (int cb = 0; cb < C::CB; ++cb)
+                        *reinterpret_cast<bf16x4 *>(dst + 16 * cb) = __builtin_convertvector(acc[cb] * inv, bf16x4);
+                    if (LSE && g == 0) LSE[m_head0[st] + n] = lse_piece;
+                }
+            } else {
+                // normalised partial output and log-sum-exp to slot
+                // (segment + workgroup), merged by the merge kernel
+                const size_t slot = (size_t)seg + w;
+                if (n < gblk) {
+                    float *dst = ws_o + (slot * GB + n) * D + 4 * g;
+#pragma unroll
+                    for (int cb = 0; cb < C::CB; ++cb) *reinterpret_cast<f32x4 *>(dst + 16 * cb) = acc[cb] * inv;
+                    if (g == 0) ws_lse[slot * GB + n] = lse_piece;
+                }
             }
         }
     };
@@ -442,86 +554,50 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
         return true;
     };
     for (;;) {
-        if (!step(0)) return;
-        if (!step(1)) return;
+        if (!step(0)) break;
+        if (!step(1)) break;
         if constexpr (NST > 2) {
-            if (!step(2)) return;
+            if (!step(2)) break;
         }
         if constexpr (NST > 3) {
-            if (!step(3)) return;
+            if (!step(3)) break;
         }
     }
 }
 
-// Combines the partial results of each segment: lse = ln sum_w exp(lse_w),
-// o = sum_w exp(lse_w - lse) o_w, over the workgroups w whose ranges touch the
-// segment.  One workgroup per segment.
+// Merges the partial results of every segment that several ranges share
+// (segments inside one range were written directly by the split kernel,
+// empty sequences too).  One single-wave workgroup per segment.
 template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(
+__global__ __launch_bounds__(64) void decode_merge_kernel(
     const float *__restrict__ ws_o, const float *__restrict__ ws_lse, const int32_t *__restrict__ seq_lens,
     __bf16 *__restrict__ O, float *__restrict__ LSE, int B, int Hq, int Hkv, int Lmax, int nhb, int n_wg)
 {
-    const int seg = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int seg = blockIdx.x, lane = threadIdx.x;
     const int G = Hq / Hkv;
     const int GB = G < 16 ? G : 16;
     const int nsub = Hkv * nhb;
     const int b = seg / nsub, sub = seg - b * nsub;
-    const int hk = sub / nhb, hb = sub - hk * nhb;
-    const int gblk = G - 16 * hb < 16 ? G - 16 * hb : 16;
-    const size_t head0 = (size_t)b * Hq + hk * G + 16 * hb;
-
-    // prefix of the segment and the batch total (every wave computes them)
+    // batch total and the prefix of sequence b
     long long T = 0, Pb = 0;
+    int Lb = 0;
     for (int pb = 0; pb < B; pb += 64) {
         const int L = pb + lane < B ? clamp_len(seq_lens[pb + lane], Lmax) : 0;
-        const int s = wave_incl_scan(L, lane);
-        if (b >= pb && b < pb + 64) Pb = T + __builtin_amdgcn_readlane(s, b - pb) - __builtin_amdgcn_readlane(L, b - pb);
-        T += __builtin_amdgcn_readlane(s, 63);
+        const int incl = wave_incl_scan(L, lane);
+        if (b >= pb && b < pb + 64) {
+            Lb = __builtin_amdgcn_readlane(L, b - pb);
+            Pb = T + __builtin_amdgcn_readlane(incl, b - pb) - Lb;
+        }
+        T += __builtin_amdgcn_readlane(incl, 63);
     }
+    if (Lb == 0) return;
     T *= nsub;
-    const int Lb = clamp_len(seq_lens[b], Lmax);
-    constexpr int C4 = D / 4;
-    if (Lb == 0) {  // no visible key: O = 0, LSE = -inf
-        for (int idx = tid; idx < gblk * C4; idx += 256) {
-            const int h = idx / C4, c4 = idx - h * C4;
-            *reinterpret_cast<bf16x4 *>(O + (head0 + h) * D + 4 * c4) = bf16x4{};
-            if (c4 == 0 && LSE) LSE[head0 + h] = -INFINITY;
-        }
-        return;
-    }
     const long long S0 = Pb * nsub + (long long)sub * Lb, S1 = S0 + Lb;
-    const int w0 = (int)(((S0 + 1) * n_wg - 1) / T);
-    const int w1 = (int)((S1 * n_wg - 1) / T);
-    for (int idx = tid; idx < gblk * C4; idx += 256) {
-        const int h = idx / C4, c4 = idx - h * C4;
-        // one pass with a running maximum; workgroups with empty ranges
-        // wrote nothing and are skipped
-        float M = -INFINITY, sum = 0.f;
-        f32x4 o = f32x4{};
-        long long lo = range_start(w0, T, n_wg);
-        for (int wg = w0; wg <= w1; ++wg) {
-            const long long hi = range_start(wg + 1, T, n_wg);
-            if (lo < hi) {
-                const size_t slot = (size_t)seg + wg;
-                const float l = ws_lse[slot * GB + h];
-                const f32x4 ov = *reinterpret_cast<const f32x4 *>(ws_o + (slot * GB + h) * D + 4 * c4);
-                if (l > M) {
-                    const float r = __expf(M - l);
-                    sum *= r;
-                    o *= r;
-                    M = l;
-                }
-                const float e = __expf(l - M);
-                sum += e;
-                o += e * ov;
-            }
-            lo = hi;
-        }
-        o *= 1.f / sum;
-        *reinterpret_cast<bf16x4 *>(O + (head0 + h) * D + 4 * c4) = __builtin_convertvector(o, bf16x4);
-        if (c4 == 0 && LSE) LSE[head0 + h] = M + __logf(sum);
-    }
+    const int w0 = (int)(((S0 + 1) * n_wg - 1) / T), w1 = (int)((S1 * n_wg - 1) / T);
+    if (w0 == w1) return;
+    const int hk = sub / nhb, hb = sub - hk * nhb;
+    const int gblk = G - 16 * hb < 16 ? G - 16 * hb : 16;
+    merge_segment<D>(ws_o, ws_lse, O, LSE, seg, w0, w1, (size_t)b * Hq + hk * G + 16 * hb, gblk, GB, T, n_wg, lane);
 }
 
 template <int D, int QR, int NST>
@@ -548,11 +624,11 @@ hipError_t launch_cfg(const DecodeArgs &a, hipStream_t stream) {
     if (n_wg > a.max_wg) n_wg = a.max_wg;
     const float sl2 = a.scale * LOG2E;
     hipLaunchKernelGGL((decode_chunk_kernel<D, QR, NST>), dim3(n_wg), dim3(64), lds_bytes, stream,
-                       (const __bf16 *)a.q, (const __bf16 *)a.k_cache, (const __bf16 *)a.v_cache, a.seq_lens, a.ws_o,
-                       a.ws_lse, a.B, a.Hq, a.Hkv, a.Lmax, a.nhb, n_wg, sl2);
+                       (const __bf16 *)a.q, (const __bf16 *)a.k_cache, (const __bf16 *)a.v_cache, a.seq_lens,
+                       (__bf16 *)a.o, a.lse, a.ws_o, a.ws_lse, a.B, a.Hq, a.Hkv, a.Lmax, a.nhb, n_wg, sl2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.B * a.Hkv * a.nhb), dim3(256), 0, stream, a.ws_o, a.ws_lse,
+    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.B * a.Hkv * a.nhb), dim3(64), 0, stream, a.ws_o, a.ws_lse,
                        a.seq_lens, (__bf16 *)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Lmax, a.nhb, n_wg);
     return hipGetLastError();
 }

@@ -87,15 +87,19 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 
 /*
  * attn_decode_workspace_bytes -- bytes of device workspace attn_decode needs
- * for these sizes: fp32 partial outputs and partial LSEs of every
- * (sequence, query head, key split).  keys_per_split as for attn_decode
- * (0 = library default).  Returns 0 for invalid sizes.
+ * for these sizes and this keys_per_split (see attn_decode).  Layout:
+ *   fp32 partial outputs  [S, min(G, 16), d]
+ *   fp32 partial LSEs     [S, min(G, 16)]   (from the next 256-byte boundary)
+ * with G = Hq / Hkv and S = B * Hkv * ceil(G / 16) + W - 1, where W is the
+ * number of split workgroups: ceil(B * Hkv * ceil(G / 16) * max_seq_len /
+ * keys_per_split) clamped to [1, 2048], or 2048 when keys_per_split is 0.
+ * Returns 0 for invalid sizes.
  */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_seq_len,
                                    int d, int keys_per_split);
 
 /*
- * attn_decode -- one decode step per sequence against a KV cache (split-KV).
+ * attn_decode -- one decode step per sequence against a KV cache.
  *
  *   q        [B, Hq, d]                 dtype (read): the new token's queries
  *   k_cache  [B, Hkv, max_seq_len, d]   dtype (read)
@@ -113,14 +117,16 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_seq_len,
  * Query head h of sequence b attends, without a mask, to the first
  * seq_lens[b] rows of K/V head h / (Hq / Hkv); this equals the last row of
  * causal attn_fwd over those rows.  The cache is not appended to.
- * The keys of each (b, K/V head) are cut into splits of keys_per_split rows
- * (0 = default 256; otherwise a multiple of 64 in [64, 65536]); each split
- * produces a partial result that a second kernel merges through the partial
- * log-sum-exps.  Only dtype ATTN_BF16 is implemented; Hq / Hkv must be at
- * most 16.
+ * The valid keys of all (sequence, K/V head, block of 16 query heads) are
+ * laid end to end and cut into W equal ranges, one per workgroup; the
+ * partial results of blocks that several ranges share are merged through
+ * their log-sum-exps by a second kernel.  keys_per_split = 0 lets the library
+ * pick W (as many workgroups as the device holds at once); a positive value
+ * asks for ranges of about that many keys of the max_seq_len-sized cache.
+ * Only dtype ATTN_BF16 is implemented; any Hq / Hkv is supported.
  *
  * Sizes: B >= 0 (0 is a no-op), Hq >= 1, Hkv >= 1, Hq % Hkv == 0,
- * max_seq_len >= 0, d in {64, 128}.
+ * max_seq_len >= 0, d in {64, 128}, keys_per_split >= 0.
  */
 int attn_decode(const void *q, const void *k_cache, const void *v_cache,
                 const int32_t *seq_lens, void *o, float *lse, int B, int Hq,

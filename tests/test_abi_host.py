@@ -98,7 +98,7 @@ def test_decode_validation(kw, status):
 def _ws_bytes(B, Hq, Hkv, Lmax, d, kps):
     """The workspace size the header documents: slots of min(G, 16) heads,
     one per (sequence, K/V head, block of 16 query heads) plus one per split
-    workgroup beyond the first; fp32 outputs (256-byte aligned), then fp32
+    workgroup beyond the first; fp32 outputs, then (256-byte aligned) fp32
     LSEs."""
     G = Hq // Hkv
     nhb = -(-G // 16)

@@ -128,12 +128,18 @@ def test_run_twice_bitwise():
 
 
 def test_workspace_reuse_and_explicit_buffer(orc):
-    sl, q, kc, vc = I.decode_inputs(4, 32, 8, 512, 128, "bf16", seed=97, lo=100, hi=512)
-    need = E.attn_decode_workspace_bytes(4, 32, 8, 512, 128)
-    ws = torch.full((need,), 0x7f, dtype=torch.uint8, device="cuda")  # garbage contents
-    o, lse = E.attn_decode(dev(q), dev(kc), dev(vc), dev(sl), workspace=ws)
-    torch.cuda.synchronize()
-    o_ref, l_ref = orc.decode(I.to_f64(q), I.to_f64(kc), I.to_f64(vc), sl.numpy(), 1 / np.sqrt(128))
-    assert_close("explicit workspace O", I.to_f64(o), o_ref, TOL_O["bf16"])
+    """One workspace filled with garbage serves calls of different sizes in
+    turn; a buffer one word short is refused."""
+    need = max(E.attn_decode_workspace_bytes(4, 32, 8, 512, 128), E.attn_decode_workspace_bytes(9, 16, 2, 300, 64))
+    ws = torch.full((need,), 0x7f, dtype=torch.uint8, device="cuda")
+    for args, seed in [((4, 32, 8, 512, 128), 97), ((9, 16, 2, 300, 64), 98), ((4, 32, 8, 512, 128), 99)]:
+        B, Hq, Hkv, Lmax, d = args
+        sl, q, kc, vc = I.decode_inputs(B, Hq, Hkv, Lmax, d, "bf16", seed=seed, lo=1, hi=Lmax)
+        o, lse = E.attn_decode(dev(q), dev(kc), dev(vc), dev(sl), workspace=ws)
+        torch.cuda.synchronize()
+        o_ref, l_ref = orc.decode(I.to_f64(q), I.to_f64(kc), I.to_f64(vc), sl.numpy(), 1 / np.sqrt(d))
+        assert_close("shared workspace O %s" % (args,), I.to_f64(o), o_ref, TOL_O["bf16"])
+        assert_close("shared workspace LSE %s" % (args,), I.to_f64(lse), l_ref, TOL_LSE)
+    small = E.attn_decode_workspace_bytes(4, 32, 8, 512, 128)
     with pytest.raises(E.AttnError):
-        E.attn_decode(dev(q), dev(kc), dev(vc), dev(sl), workspace=ws[: need - 16])
+        E.attn_decode(dev(q), dev(kc), dev(vc), dev(sl), workspace=ws[: small - 16])
