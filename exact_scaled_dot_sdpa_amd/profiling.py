@@ -1,6 +1,7 @@
 """Summaries of rocprofv3 output for the profiles/ folder.
 
-    python -m exact_scaled_dot_sdpa_amd.profiling stats KERNEL_STATS_CSV --cmd "..." --out FILE.md
+    python -m exact_scaled_dot_sdpa_amd.profiling stats KERNEL_STATS_CSV --cmd "..." --out FILE.md \
+        [--trace KERNEL_TRACE_CSV --last N]
     python -m exact_scaled_dot_sdpa_amd.profiling traffic --fetch FETCH_CSV --write WRITE_CSV \
         --calib-mib 512 --cmd-fetch "..." --cmd-write "..." --json profiles/traffic.json --out FILE.md
 
@@ -22,19 +23,34 @@ import sys
 KERNELS = {
     # logical kernel -> substrings of the dispatched kernel names that make one launch
     "prefill": ["prefill_bf16_kernel"],
-    "decode": ["decode_split_kernel", "decode_merge_kernel"],
+    "decode": ["decode_chunk_kernel", "decode_merge_kernel"],
 }
 COPY_KERNEL = "copyBuffer"
 
 
 def _short(name):
-    for key in ("prefill_bf16_kernel", "prefill_f32_kernel", "decode_split_kernel", "decode_merge_kernel"):
+    for key in ("prefill_bf16_kernel", "prefill_f32_kernel", "decode_chunk_kernel", "decode_merge_kernel"):
         if key in name:
             return key
     return name[:60]
 
 
-def stats(path, cmd, out):
+def _last_n_means(trace_csv, n):
+    """Average duration (us) of the last n dispatches of each kernel in a
+    rocprofv3 kernel_trace csv (the timed steps, after the warm-up ones)."""
+    per = {}
+    for r in csv.DictReader(open(trace_csv)):
+        per.setdefault(r["Kernel_Name"], []).append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    res = {}
+    for name, v in per.items():
+        v.sort()
+        last = [d for _, d in v[-n:]]
+        res[name] = (len(last), sum(last) / len(last) / 1e3)
+    return res
+
+
+def stats(path, cmd, out, trace=None, last=0):
     rows = list(csv.DictReader(open(path)))
     lines = ["# rocprofv3 kernel statistics", "", "Command:", "", "```", cmd, "```", "",
              "| kernel | calls | avg (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
@@ -42,6 +58,13 @@ def stats(path, cmd, out):
         lines.append("| %s | %s | %.2f | %.2f | %.2f | %.2f%% |" % (
             _short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    if trace and last > 0:
+        means = _last_n_means(trace, last)
+        lines += ["", "Average over the last %d dispatches of each kernel (the timed steps; the table above "
+                      "also counts the warm-up dispatches):" % last, "",
+                  "| kernel | dispatches | avg (us) |", "|---|---|---|"]
+        for name, (cnt, avg) in sorted(means.items(), key=lambda kv: -kv[1][1]):
+            lines.append("| %s | %d | %.2f |" % (_short(name), cnt, avg))
     lines += ["", "Full kernel names:", ""] + ["- `%s`" % r["Name"] for r in rows]
     text = "\n".join(lines) + "\n"
     with open(out, "w") as f:
@@ -128,6 +151,8 @@ def main(argv=None):
     s.add_argument("csv")
     s.add_argument("--cmd", required=True)
     s.add_argument("--out", required=True)
+    s.add_argument("--trace", default=None, help="kernel_trace csv of the same run")
+    s.add_argument("--last", type=int, default=0, help="also average the last N dispatches per kernel")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -138,7 +163,7 @@ def main(argv=None):
     t.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.what == "stats":
-        print(stats(a.csv, a.cmd, a.out))
+        print(stats(a.csv, a.cmd, a.out, a.trace, a.last))
     else:
         print(traffic(a.fetch, a.write, a.calib_mib, a.cmd_fetch, a.cmd_write, a.json, a.out))
 
