@@ -28,7 +28,9 @@
 //     or range).  The K and V rows of a chunk, and the query rows of its
 //     segment, go from HBM straight into LDS with buffer_load ... lds (1 KB per
 //     instruction); a ring of NST stages keeps NST-1 chunks in flight while one
-//     is computed.  The buffer descriptor of each load ends at the last valid
+//     is computed.  Each stage is its own LDS array, which lets the compiler
+//     see that a stage's reads wait only for that stage's loads (with one
+//     array it waits for every load in flight before each read).  The buffer descriptor of each load ends at the last valid
 //     row, so rows at or beyond seq_lens[b] are never read: the hardware range
 //     check returns zeros for them.
 //   * Scores S = K Q^T on v_mfma_f32_16x16x32_bf16: the 16 keys of a half-chunk
@@ -245,7 +247,13 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
 {
     using C = DC<D>;
     using S = Stage<D, QR>;
-    extern __shared__ __attribute__((aligned(1024))) char lds[];
+    // one LDS array per stage: the compiler then knows which in-flight
+    // LDS-DMA a stage's reads depend on instead of waiting for all of them
+    __shared__ __attribute__((aligned(1024))) char lds0[S::BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds1[S::BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds2[NST > 2 ? S::BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char lds3[NST > 3 ? S::BYTES : 16];
+    auto stage = [&](int st) { return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : lds3; };
 
     const int lane = threadIdx.x;
     const int w = blockIdx.x;
@@ -348,7 +356,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
             cur_w1 = (int)((S1 * n_wg - 1) / T);
         }
         const size_t row0 = (size_t)(b * Hkv + hk) * Lmax + key;
-        dma_chunk<D, QR>(lds + st * S::BYTES, Kc + row0 * D, Vc + row0 * D,
+        dma_chunk<D, QR>(stage(st), Kc + row0 * D, Vc + row0 * D,
                          Q + ((size_t)b * Hq + hk * G + 16 * hb) * D, cnt * D * 2, gblk * D * 2, voff_k, voff_v);
         m_seg[st] = b * nsub + sub;
         m_cnt[st] = cnt;
@@ -413,7 +421,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
     float m_ref = 0.f, l_run = 0.f;
 
     auto compute = [&](const int st) {
-        const char *src = lds + st * S::BYTES;
+        const char *src = stage(st);
         const int cnt = m_cnt[st];
         // operands
         bf16x8 qb[C::KS];
@@ -602,8 +610,6 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
 
 template <int D, int QR, int NST>
 hipError_t launch_cfg(const DecodeArgs &a, hipStream_t stream) {
-    using S = Stage<D, QR>;
-    const size_t lds_bytes = (size_t)NST * S::BYTES;
     int n_wg = a.n_wg;
     if (n_wg <= 0) {
         // as many single-wave workgroups as the chip holds at once
@@ -614,8 +620,7 @@ hipError_t launch_cfg(const DecodeArgs &a, hipStream_t stream) {
             int cus = 0, per_cu = 0;
             hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
             if (e != hipSuccess) return e;
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_chunk_kernel<D, QR, NST>, 64,
-                                                             lds_bytes);
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_chunk_kernel<D, QR, NST>, 64, 0);
             if (e != hipSuccess) return e;
             cached[dev] = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
         }
@@ -623,7 +628,7 @@ hipError_t launch_cfg(const DecodeArgs &a, hipStream_t stream) {
     }
     if (n_wg > a.max_wg) n_wg = a.max_wg;
     const float sl2 = a.scale * LOG2E;
-    hipLaunchKernelGGL((decode_chunk_kernel<D, QR, NST>), dim3(n_wg), dim3(64), lds_bytes, stream,
+    hipLaunchKernelGGL((decode_chunk_kernel<D, QR, NST>), dim3(n_wg), dim3(64), 0, stream,
                        (const __bf16 *)a.q, (const __bf16 *)a.k_cache, (const __bf16 *)a.v_cache, a.seq_lens,
                        (__bf16 *)a.o, a.lse, a.ws_o, a.ws_lse, a.B, a.Hq, a.Hkv, a.Lmax, a.nhb, n_wg, sl2);
     hipError_t e = hipGetLastError();
