@@ -38,6 +38,7 @@ def _bind(path):
     lib.oracle_blockwise.argtypes = [_dp, _dp, _dp, _dp, _dp] + [c_int] * 6 + [c_double, c_int, c_int, c_int]
     lib.oracle_blockwise.restype = c_int
     lib.oracle_decode.argtypes = [_dp, _dp, _dp, _ip, _dp, _dp] + [c_int] * 5 + [c_double, c_int]
+    lib.oracle_decode_paged.argtypes = [_dp, _dp, _dp, _ip, _ip, _dp, _dp] + [c_int] * 7 + [c_double, c_int]
     lib.oracle_decode.restype = c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = c_int
@@ -148,6 +149,32 @@ class Oracle:
             raise RuntimeError("oracle_decode failed")
         return o, lse
 
+    def decode_paged(self, q, k_pages, v_pages, block_table, seq_lens, scale, nthreads=0):
+        """One-token decode against a paged cache.  q [B,Hq,d], pages
+        [num_blocks,Hkv,block_size,d], block_table int32 [B,max_blocks],
+        seq_lens [B].  Returns (o [B,Hq,d], lse [B,Hq])."""
+        if q.ndim != 3 or k_pages.ndim != 4 or k_pages.shape != v_pages.shape:
+            raise ValueError("paged decode shapes: q [B,Hq,d], pages [num_blocks,Hkv,block_size,d]")
+        B, Hq, d = q.shape
+        nb, Hkv, bs, dk = k_pages.shape
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        if dk != d or Hq % Hkv or bt.ndim != 2 or bt.shape[0] != B:
+            raise ValueError("paged decode shape mismatch")
+        q, qp = _f64(q)
+        kpg, kpp = _f64(k_pages)
+        vpg, vpp = _f64(v_pages)
+        sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        if sl.shape != (B,):
+            raise ValueError("seq_lens must be [B]")
+        o = np.zeros((B, Hq, d))
+        lse = np.zeros((B, Hq))
+        rc = self.lib.oracle_decode_paged(qp, kpp, vpp, bt.ctypes.data_as(_ip), sl.ctypes.data_as(_ip),
+                                          o.ctypes.data_as(_dp), lse.ctypes.data_as(_dp), B, Hq, Hkv, nb, bs,
+                                          bt.shape[1], d, float(scale), int(nthreads))
+        if rc:
+            raise RuntimeError("oracle_decode_paged failed")
+        return o, lse
+
 
 _default = None
 
@@ -183,3 +210,7 @@ def blockwise(*a, **kw):
 
 def decode(*a, **kw):
     return default().decode(*a, **kw)
+
+
+def decode_paged(*a, **kw):
+    return default().decode_paged(*a, **kw)

@@ -185,6 +185,69 @@ static void set_threads(int nthreads)
 #endif
 }
 
+
+/* One decode step per sequence against a paged KV cache ("Transformer 笔记：
+ * 注意力机制为什么会变成系统问题", the FlashAttention / PagedAttention section,
+ * and the pwwt.cn blog, sec. 3.3: the cache is cut into fixed-size blocks
+ * placed anywhere in a pool).  Pool layout kp/vp [num_blocks, Hkv, bs, d];
+ * logical row j of sequence b lives in physical block
+ * block_table[b * max_blocks + j / bs], row j % bs.  seq_lens[b] is clamped
+ * to [0, max_blocks * bs] and table entries to [0, num_blocks - 1]
+ * (num_blocks == 0: every sequence is empty).  The rows of each (b, KV head)
+ * are gathered into a contiguous buffer and attended exactly as in
+ * oracle_decode. */
+int oracle_decode_paged(const double *q, const double *kp, const double *vp,
+                        const int32_t *block_table, const int32_t *seq_lens,
+                        double *o, double *lse, int B, int Hq, int Hkv,
+                        int num_blocks, int bs, int max_blocks, int d,
+                        double scale, int nthreads)
+{
+    if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || num_blocks < 0 || bs < 1 ||
+        max_blocks < 0 || d < 1)
+        return -1;
+    set_threads(nthreads);
+    const long G = Hq / Hkv;
+    const long Lmax = num_blocks > 0 ? (long)max_blocks * bs : 0;
+    const long rows = (long)B * Hq;
+    int bad = 0;
+#pragma omp parallel
+    {
+        const size_t n = (size_t)(Lmax > 0 ? Lmax : 1);
+        double *s = (double *)malloc(sizeof(double) * n);
+        double *K = (double *)malloc(sizeof(double) * n * (size_t)d);
+        double *V = (double *)malloc(sizeof(double) * n * (size_t)d);
+        if (!s || !K || !V) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long r = 0; r < rows; ++r) {
+            if (!s || !K || !V)
+                continue;
+            long b = r / Hq, h = r % Hq, hk = h / G;
+            long L = seq_lens[b];
+            if (L < 0)
+                L = 0;
+            if (L > Lmax)
+                L = Lmax;
+            for (long j = 0; j < L; ++j) {
+                long blk = block_table[b * (long)max_blocks + j / bs];
+                if (blk < 0)
+                    blk = 0;
+                if (blk > num_blocks - 1)
+                    blk = num_blocks - 1;
+                const long src = ((blk * Hkv + hk) * (long)bs + j % bs) * d;
+                memcpy(K + j * d, kp + src, sizeof(double) * (size_t)d);
+                memcpy(V + j * d, vp + src, sizeof(double) * (size_t)d);
+            }
+            direct_row(q + r * d, K, V, L, d, scale, s, o + r * d, lse + r, NULL);
+        }
+        free(s);
+        free(K);
+        free(V);
+    }
+    return bad ? -1 : 0;
+}
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

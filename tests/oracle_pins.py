@@ -320,6 +320,64 @@ def pin_decode_is_last_row(orc):
     _close(o3[1], o4[0], 0.0, "seq_len above Lmax clamps to Lmax")
 
 
+def pin_paged_decode(orc):
+    """[N] (FlashAttention / PagedAttention section) and [E] sec. 3.3: a paged
+    cache stores each sequence's K/V in fixed-size blocks anywhere in a pool,
+    found through a block table.  Decode over the pages must equal decode
+    over the same rows laid out contiguously, whatever the block order;
+    sequences may share prefix blocks; unused blocks are never read; table
+    entries and lengths are clamped as documented."""
+    rng = _rng(13)
+    B, Hq, Hkv, d, bs, nblk, maxb = 4, 6, 2, 8, 4, 24, 5
+    kp = _randn(rng, nblk, Hkv, bs, d)
+    vp = _randn(rng, nblk, Hkv, bs, d)
+    q = _randn(rng, B, Hq, d)
+    bt = rng.permutation(nblk)[:B * maxb].reshape(B, maxb).astype(np.int32)
+    bt[1, :2] = bt[0, :2]  # sequence 1 shares its first two blocks with sequence 0
+    sl = np.array([20, 9, 1, 0], dtype=np.int32)
+
+    def contiguous(table):
+        Lmax = maxb * bs
+        kc = np.zeros((B, Hkv, Lmax, d))
+        vc = np.zeros((B, Hkv, Lmax, d))
+        for b in range(B):
+            for j in range(Lmax):
+                blk = min(max(int(table[b, j // bs]), 0), nblk - 1)
+                kc[b, :, j] = kp[blk, :, j % bs]
+                vc[b, :, j] = vp[blk, :, j % bs]
+        return kc, vc
+
+    o, lse = orc.decode_paged(q, kp, vp, bt, sl, 0.4)
+    kc, vc = contiguous(bt)
+    oc, lc = orc.decode(q, kc, vc, sl, 0.4)
+    _close(o, oc, 0.0, "paged decode == contiguous decode")
+    _close(lse, lc, 0.0, "paged decode lse == contiguous decode lse")
+    # blocks no valid row lives in are never read
+    used = {int(bt[b, j // bs]) for b in range(B) for j in range(int(sl[b]))}
+    kpp, vpp = kp.copy(), vp.copy()
+    for blk in range(nblk):
+        if blk not in used:
+            kpp[blk] = np.nan
+            vpp[blk] = np.nan
+    o2, l2 = orc.decode_paged(q, kpp, vpp, bt, sl, 0.4)
+    _close(o2, o, 0.0, "paged decode ignores unused blocks")
+    # a different physical placement of the same rows gives the same result
+    perm = rng.permutation(nblk)
+    inv = np.argsort(perm)
+    o3, l3 = orc.decode_paged(q, kp[perm], vp[perm], inv[bt].astype(np.int32), sl, 0.4)
+    _close(o3, o, 0.0, "paged decode independent of block placement")
+    # clamping: lengths above max_blocks * bs, table entries out of range
+    bt2 = bt.copy()
+    bt2[0, 1] = -3
+    bt2[2, 0] = nblk + 7
+    sl2 = np.array([99, 9, 1, 0], dtype=np.int32)
+    o4, l4 = orc.decode_paged(q, kp, vp, bt2, sl2, 0.4)
+    kc4, vc4 = contiguous(bt2)
+    oc4, lc4 = orc.decode(q, kc4, vc4, np.minimum(sl2, maxb * bs), 0.4)
+    _close(o4, oc4, 0.0, "paged decode clamps lengths and table entries")
+    _close(l4, lc4, 0.0, "paged decode clamps (lse)")
+
+
 def pin_blockwise_equals_direct(orc):
     """[R] sec. 6.3 / [IO] eqs. (1)-(2): the blockwise recurrence reaches the
     direct result, for any block size, dividing or not."""
@@ -362,6 +420,7 @@ ALL_PINS = [
     pin_gqa_repeat,
     pin_chunked_prefill_alignment,
     pin_decode_is_last_row,
+    pin_paged_decode,
     pin_blockwise_equals_direct,
     pin_rows_entry_matches_full,
 ]

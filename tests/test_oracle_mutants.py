@@ -34,6 +34,10 @@ MUTANTS = [
     ("decode_drops_last_row", [("direct_row(q + r * d, K, V, L,", "direct_row(q + r * d, K, V, L > 0 ? L - 1 : 0,")]),
     ("decode_no_clamp", [("if (L > Lmax)\n                L = Lmax;", "")]),
     ("decode_wrong_head", [("long b = r / Hq, h = r % Hq, hk = h / G;", "long b = r / Hq, h = r % Hq, hk = h % Hkv;")]),
+    ("paged_row_offset", [("* (long)bs + j % bs) * d;", "* (long)bs + j / bs) * d;")]),
+    ("paged_head_major", [("const long src = ((blk * Hkv + hk)", "const long src = ((hk * num_blocks + blk)")]),
+    ("paged_block_index", [("block_table[b * (long)max_blocks + j / bs]", "block_table[b * (long)max_blocks + j % max_blocks]")]),
+    ("paged_no_entry_clamp", [("if (blk > num_blocks - 1)\n                    blk = num_blocks - 1;", "")]),
 ]
 
 
