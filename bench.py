@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-paged]
 
 One step is one pass of the whole path over synthetic inputs already resident
 in device memory:
@@ -17,7 +17,9 @@ FLOPs: 4*d per visible query/key pair), the decode bandwidth in GB/s (valid
 cache rows plus q, o, lse) in `decode`, and for each kernel its roofline
 fraction from its average duration measured with HIP events on the stream the
 kernels run on.  `cpu_baseline` times the fp64 oracle on a bounded sample of the
-prefill rows on the host cores.
+prefill rows on the host cores.  `decode_paged` times the decode workload
+against a paged cache (block table over a shuffled pool) on its own, after the
+timed steps.
 """
 import argparse
 import json
@@ -46,6 +48,8 @@ def parse():
                     help="also run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="run one kernel only (for profiling runs)")
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache decode measurement")
+    ap.add_argument("--paged-block-size", type=int, default=64)
     return ap.parse_args()
 
 
@@ -64,6 +68,43 @@ def stored_traffic(kernel):
     if e is None or e.get("source_digest") != source_digest(kernel):
         return None
     return e.get("bytes_per_launch")
+
+
+def paged_decode_line(E, A, I, dev, block_size, reps=4, steps=20, warmup=50):
+    """The decode workload's shape in a paged cache (shuffled pool of
+    block_size-row blocks), timed on its own after the main loop."""
+    import torch
+
+    wd = I.WORKLOADS["C5"]
+    sl, q, kp, vp, bt = I.paged_decode_inputs(wd.B, wd.Hq, wd.Hkv, wd.d, block_size, wd.Lmax // block_size,
+                                              wd.dtype, seed=wd.seed, lo=wd.lo, hi=wd.hi)
+    pools = [(kp.to(dev), vp.to(dev)) for _ in range(reps)]
+    q, sl_d, bt = q.to(dev), sl.to(dev), bt.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    ws = torch.empty(E.attn_decode_workspace_bytes(wd.B, wd.Hq, wd.Hkv, wd.Lmax, wd.d), dtype=torch.uint8,
+                     device=dev)
+
+    def call(i):
+        k_p, v_p = pools[i % reps]
+        E.attn_decode_paged(q, k_p, v_p, bt, sl_d, scale=wd.scale, o=o, lse=lse, workspace=ws)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        call(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(steps)) / steps
+    by = A.decode_bytes(sl.tolist(), wd.Hq, wd.Hkv, wd.d, wd.dtype)
+    return {"value": round(by / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "frac_hbm": round(by / (ms * 1e-3) / 1e9 /
+            PEAK_HBM_GBS, 4), "avg_launch_ms": round(ms, 5), "block_size": block_size,
+            "sum_seq_len": int(sl.sum()), "bytes_per_launch": by,
+            "note": "same shape and lengths as the decode workload, rows in a shuffled pool of blocks"}
 
 
 def cpu_baseline(q, k, v, w, target_s):
@@ -240,6 +281,8 @@ def main():
             "frac": round(d_gbs / PEAK_HBM_GBS, 4), "traffic": tr,
             "kernel": "decode_chunk_kernel<128,4,3> + decode_merge_kernel<128>", "avg_launch_ms": round(d_ms, 5),
         }
+    if run_d and not args.no_paged:
+        out["decode_paged"] = paged_decode_line(E, A, I, dev, args.paged_block_size)
     if not args.no_cpu_baseline and run_p:
         out["cpu_baseline"] = cpu_baseline(q_cpu, k_cpu, v_cpu, wp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

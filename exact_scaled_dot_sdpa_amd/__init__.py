@@ -10,6 +10,8 @@ Functions carry the names of the C entry points:
     attn_fwd(q, k, v, scale=None, causal=False, o=None, lse=None, return_lse=True)
     attn_decode(q, k_cache, v_cache, seq_lens, scale=None, o=None, lse=None,
                 workspace=None, keys_per_split=0, return_lse=True)
+    attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, o=None,
+                      lse=None, workspace=None, keys_per_split=0, return_lse=True)
     attn_decode_workspace_bytes(B, Hq, Hkv, max_seq_len, d, keys_per_split=0)
     attn_status_str(status)
 
@@ -26,6 +28,7 @@ from ._binding import (  # noqa: F401
     ATTN_OK,
     AttnError,
     attn_decode,
+    attn_decode_paged,
     attn_decode_workspace_bytes,
     attn_fwd,
     attn_status_str,
@@ -36,6 +39,7 @@ from ._binding import (  # noqa: F401
 __all__ = [
     "attn_fwd",
     "attn_decode",
+    "attn_decode_paged",
     "attn_decode_workspace_bytes",
     "attn_status_str",
     "AttnError",

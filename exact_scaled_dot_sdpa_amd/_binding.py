@@ -39,6 +39,8 @@ def lib():
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
     L.attn_decode.restype = i
+    L.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp, sz, vp]
+    L.attn_decode_paged.restype = i
     L.attn_status_str.argtypes = [i]
     L.attn_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -154,4 +156,46 @@ def attn_decode(q, k_cache, v_cache, seq_lens, scale=None, o=None, lse=None, wor
                            workspace.data_ptr(), ws_bytes, _stream_handle(q, stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode")
+    return (o, lse) if return_lse else o
+
+
+def attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, o=None, lse=None, workspace=None,
+                      keys_per_split=0, return_lse=True, stream=None):
+    """One decode step against a paged cache: q [B,Hq,d], pools k_pages /
+    v_pages [num_blocks,Hkv,block_size,d] (bf16), block_table int32
+    [B,max_blocks_per_seq] and seq_lens int32 [B] on the device.  Returns
+    (o, lse) or o."""
+    torch = _torch()
+    _check_dev("q", q)
+    _check_dev("k_pages", k_pages, q.dtype)
+    _check_dev("v_pages", v_pages, q.dtype)
+    _check_dev("block_table", block_table, torch.int32)
+    _check_dev("seq_lens", seq_lens, torch.int32)
+    if q.dim() != 3 or k_pages.dim() != 4 or k_pages.shape != v_pages.shape or block_table.dim() != 2:
+        raise ValueError("q [B,Hq,d], pools [num_blocks,Hkv,block_size,d], block_table [B,max_blocks] expected")
+    B, Hq, d = q.shape
+    nb, Hkv, bs, dk = k_pages.shape
+    if dk != d or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("paged decode shape mismatch")
+    mb = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    _check_dev("o", o, q.dtype)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_dev("lse", lse, torch.float32)
+    need = attn_decode_workspace_bytes(B, Hq, Hkv, mb * bs, d, keys_per_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_dev("workspace", workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().attn_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
+                                 seq_lens.data_ptr(), o.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                 B, Hq, Hkv, nb, bs, mb, d, float(scale), int(keys_per_split), _dtype_code(q),
+                                 workspace.data_ptr(), ws_bytes, _stream_handle(q, stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_paged")
     return (o, lse) if return_lse else o

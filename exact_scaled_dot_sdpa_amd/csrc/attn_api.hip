@@ -95,34 +95,69 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_seq_len, int 
     return total;
 }
 
-int attn_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens, void *o,
-                float *lse, int B, int Hq, int Hkv, int max_seq_len, int d, float scale, int keys_per_split,
-                int dtype, void *workspace, size_t workspace_bytes, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+// Shared body of attn_decode and attn_decode_paged; the paged cache passes
+// block_table != nullptr and Lmax = max_blocks * block_size.
+int decode_call(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens, void *o, float *lse,
+                int B, int Hq, int Hkv, int Lmax, int d, float scale, int keys_per_split, int dtype,
+                void *workspace, size_t workspace_bytes, hipStream_t stream, const int32_t *block_table,
+                int block_size, int max_blocks, int num_blocks)
 {
-    if (!decode_sizes_ok(B, Hq, Hkv, max_seq_len)) return ATTN_ERR_INVALID_ARG;
+    if (!decode_sizes_ok(B, Hq, Hkv, Lmax)) return ATTN_ERR_INVALID_ARG;
     if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
     if (keys_per_split < 0) return ATTN_ERR_INVALID_ARG;
     if (!supported_d(d) || dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
     if (B == 0) return ATTN_OK;
-    if (!q || !o || !seq_lens || (max_seq_len > 0 && (!k_cache || !v_cache))) return ATTN_ERR_INVALID_ARG;
+    if (!q || !o || !seq_lens || (Lmax > 0 && (!k_cache || !v_cache))) return ATTN_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(o, 16) || !aligned(seq_lens, 4) || (k_cache && !aligned(k_cache, 16)) ||
         (v_cache && !aligned(v_cache, 16)))
         return ATTN_ERR_INVALID_ARG;
     if (lse && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARG;
-    const DecodePlan p = decode_plan(B, Hq, Hkv, max_seq_len, keys_per_split);
+    const DecodePlan p = decode_plan(B, Hq, Hkv, Lmax, keys_per_split);
     // cache rows and segment counts stay in 32-bit arithmetic
-    if ((long long)B * Hkv * max_seq_len > 0x7fffffffLL || (long long)B * Hq > 0x7fffffffLL ||
-        p.slots > 0x7fffffffLL)
-        return ATTN_ERR_UNSUPPORTED;
+    const long long rows = block_table ? (long long)num_blocks * Hkv * block_size : (long long)B * Hkv * Lmax;
+    if (rows > 0x7fffffffLL || (long long)B * Hq > 0x7fffffffLL || p.slots > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
     size_t ob, need;
     workspace_layout(p, d, &ob, &need);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_ERR_WORKSPACE;
 
-    attn::DecodeArgs a{q, k_cache, v_cache, seq_lens, o, lse, B, Hq, Hkv, max_seq_len, d, scale,
-                       p.nhb, p.n_wg, p.max_wg, (float *)workspace, (float *)((char *)workspace + ob)};
+    attn::DecodeArgs a{q, k_cache, v_cache, seq_lens, o, lse, B, Hq, Hkv, Lmax, d, scale,
+                       p.nhb, p.n_wg, p.max_wg, (float *)workspace, (float *)((char *)workspace + ob),
+                       block_table, block_size, max_blocks, num_blocks};
     const hipError_t e = attn::launch_decode_bf16(a, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens, void *o,
+                float *lse, int B, int Hq, int Hkv, int max_seq_len, int d, float scale, int keys_per_split,
+                int dtype, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return decode_call(q, k_cache, v_cache, seq_lens, o, lse, B, Hq, Hkv, max_seq_len, d, scale, keys_per_split,
+                       dtype, workspace, workspace_bytes, stream, nullptr, 0, 0, 0);
+}
+
+int attn_decode_paged(const void *q, const void *k_pages, const void *v_pages, const int32_t *block_table,
+                      const int32_t *seq_lens, void *o, float *lse, int B, int Hq, int Hkv, int num_blocks,
+                      int block_size, int max_blocks_per_seq, int d, float scale, int keys_per_split, int dtype,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (num_blocks < 0 || block_size < 1 || max_blocks_per_seq < 0) return ATTN_ERR_INVALID_ARG;
+    const long long lmax = (long long)max_blocks_per_seq * block_size;
+    if (lmax > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+    // an empty pool holds no rows: every sequence is empty
+    const int Lmax = num_blocks > 0 ? (int)lmax : 0;
+    if (Lmax > 0 && (!block_table || !aligned(block_table, 4))) return ATTN_ERR_INVALID_ARG;
+    return decode_call(q, k_pages, v_pages, seq_lens, o, lse, B, Hq, Hkv, Lmax, d, scale, keys_per_split, dtype,
+                       workspace, workspace_bytes, stream, Lmax > 0 ? block_table : nullptr, block_size,
+                       max_blocks_per_seq, num_blocks);
 }
 
 const char *attn_status_str(int status)

@@ -239,11 +239,16 @@ __device__ void merge_segment(const float *ws_o, const float *ws_lse, __bf16 *O,
     }
 }
 
+// block_table != nullptr (paged cache): Kc / Vc are a pool
+// [num_blocks, Hkv, bs, d] and row j of sequence b lives in block
+// block_table[b * max_blocks + j / bs] (entries clamped to the pool), row
+// j % bs; otherwise Kc / Vc are [B, Hkv, Lmax, d].
 template <int D, int QR, int NST>
 __global__ __launch_bounds__(64) void decode_chunk_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ Kc, const __bf16 *__restrict__ Vc,
     const int32_t *__restrict__ seq_lens, __bf16 *__restrict__ O, float *__restrict__ LSE, float *__restrict__ ws_o,
-    float *__restrict__ ws_lse, int B, int Hq, int Hkv, int Lmax, int nhb, int n_wg, float sl2)
+    float *__restrict__ ws_lse, int B, int Hq, int Hkv, int Lmax, int nhb, int n_wg, float sl2,
+    const int32_t *__restrict__ block_table, int bs, int max_blocks, int num_blocks)
 {
     using C = DC<D>;
     using S = Stage<D, QR>;
@@ -336,6 +341,20 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
     bool m_first[NST], m_last[NST];
     int cur_w0 = 0, cur_w1 = 0;  // of the segment the cursor is in
 
+    // paged cache: a page of 64 block-table entries of sequence bt_b, one per
+    // lane, reloaded when the cursor leaves it
+    int bt_b = -1, bt_base = 0, bt_page = 0;
+    auto phys_block = [&](int lb) {
+        if (b != bt_b || lb < bt_base || lb >= bt_base + 64) {
+            bt_b = b;
+            bt_base = lb & ~63;
+            const int idx = bt_base + lane;
+            bt_page = idx < max_blocks ? block_table[(size_t)b * max_blocks + idx] : 0;
+        }
+        const int p = __builtin_amdgcn_readlane(bt_page, lb - bt_base);
+        return p < 0 ? 0 : (p > num_blocks - 1 ? num_blocks - 1 : p);
+    };
+
     // Issue the loads of the next chunk of the range into stage st and
     // advance the cursor; false (nothing issued) once the range is done.
     auto issue = [&](const int st) {
@@ -355,7 +374,14 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
             cur_w0 = (int)(((S0 + 1) * n_wg - 1) / T);
             cur_w1 = (int)((S1 * n_wg - 1) / T);
         }
-        const size_t row0 = (size_t)(b * Hkv + hk) * Lmax + key;
+        size_t row0;
+        if (block_table) {  // paged: a chunk never crosses a block
+            const int lb = key / bs, off = key - lb * bs;
+            cnt = cnt < bs - off ? cnt : bs - off;
+            row0 = ((size_t)phys_block(lb) * Hkv + hk) * bs + off;
+        } else {
+            row0 = (size_t)(b * Hkv + hk) * Lmax + key;
+        }
         dma_chunk<D, QR>(stage(st), Kc + row0 * D, Vc + row0 * D,
                          Q + ((size_t)b * Hq + hk * G + 16 * hb) * D, cnt * D * 2, gblk * D * 2, voff_k, voff_v);
         m_seg[st] = b * nsub + sub;
@@ -630,7 +656,8 @@ hipError_t launch_cfg(const DecodeArgs &a, hipStream_t stream) {
     const float sl2 = a.scale * LOG2E;
     hipLaunchKernelGGL((decode_chunk_kernel<D, QR, NST>), dim3(n_wg), dim3(64), 0, stream,
                        (const __bf16 *)a.q, (const __bf16 *)a.k_cache, (const __bf16 *)a.v_cache, a.seq_lens,
-                       (__bf16 *)a.o, a.lse, a.ws_o, a.ws_lse, a.B, a.Hq, a.Hkv, a.Lmax, a.nhb, n_wg, sl2);
+                       (__bf16 *)a.o, a.lse, a.ws_o, a.ws_lse, a.B, a.Hq, a.Hkv, a.Lmax, a.nhb, n_wg, sl2,
+                       a.block_table, a.block_size, a.max_blocks, a.num_blocks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.B * a.Hkv * a.nhb), dim3(64), 0, stream, a.ws_o, a.ws_lse,

@@ -6,7 +6,8 @@ the workload's element type) and describes the workload shapes.  The HIP path
 and the oracle consume the very same rounded values.
 
 Draw order is fixed: q, k, v for prefill; seq_lens, q, k_cache, v_cache for
-decode.  seq_lens are uniform integers in [lo, hi] inclusive.
+decode; seq_lens, q, k_pages, v_pages, block order for paged decode.
+seq_lens are uniform integers in [lo, hi] inclusive.
 """
 from dataclasses import dataclass, field
 from typing import Optional
@@ -107,6 +108,30 @@ def decode_inputs(B, Hq, Hkv, Lmax, d, dtype, seed, lo=512, hi=4096,
     kc = randn((B, Hkv, Lmax, d), dtype, g)
     vc = randn((B, Hkv, Lmax, d), dtype, g)
     return seq_lens, q, kc, vc
+
+
+def paged_decode_inputs(B, Hq, Hkv, d, block_size, max_blocks, dtype, seed, lo=512, hi=4096, spare_blocks=0):
+    """A paged KV cache holding the same kind of data as ``decode_inputs``:
+    (seq_lens int32 [B], q [B,Hq,d], k_pages/v_pages [num_blocks,Hkv,block_size,d],
+    block_table int32 [B,max_blocks]) on the CPU.  The pool has exactly the
+    blocks the sequences' lengths need plus ``spare_blocks`` unused ones, in
+    a seeded random order; table entries past a sequence's last block point
+    at pool block 0 (they are never read)."""
+    g = _gen(seed)
+    Lmax = max_blocks * block_size
+    seq_lens = torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int64).clamp(max=Lmax).to(torch.int32)
+    nblk = [(int(L) + block_size - 1) // block_size for L in seq_lens]
+    num_blocks = sum(nblk) + spare_blocks
+    q = randn((B, Hq, d), dtype, g)
+    kp = randn((num_blocks, Hkv, block_size, d), dtype, g)
+    vp = randn((num_blocks, Hkv, block_size, d), dtype, g)
+    order = torch.randperm(num_blocks, generator=g).to(torch.int32)
+    table = torch.zeros((B, max_blocks), dtype=torch.int32)
+    at = 0
+    for b in range(B):
+        table[b, :nblk[b]] = order[at:at + nblk[b]]
+        at += nblk[b]
+    return seq_lens, q, kp, vp, table
 
 
 def workload_inputs(name: str, seed_offset: int = 0):

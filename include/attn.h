@@ -134,6 +134,39 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache,
                 int keys_per_split, int dtype, void *workspace,
                 size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * attn_decode_paged -- attn_decode against a paged KV cache: each sequence's
+ * cached rows live in fixed-size blocks anywhere in a pool, found through a
+ * block table ("Transformer 笔记：注意力机制为什么会变成系统问题", the
+ * FlashAttention / PagedAttention section; the pwwt.cn engineering blog,
+ * sec. 3.3).
+ *
+ *   k_pages, v_pages [num_blocks, Hkv, block_size, d]  dtype (read): the pool
+ *   block_table      [B, max_blocks_per_seq] int32, device (read): logical
+ *            block j of sequence b is pool block block_table[b][j]; entries
+ *            outside [0, num_blocks) are clamped into it (no fault, no error)
+ *   seq_lens [B] int32, device: clamped to [0, max_blocks_per_seq *
+ *            block_size]; rows at or beyond seq_lens[b] are never read, and
+ *            neither are table entries past the last valid row's block
+ *   q, o, lse, scale, keys_per_split, dtype, stream: as for attn_decode.
+ *   workspace: as for attn_decode, sized by attn_decode_workspace_bytes(B,
+ *            Hq, Hkv, max_blocks_per_seq * block_size, d, keys_per_split).
+ *
+ * Blocks may be shared between sequences (shared prefixes).  block_size is
+ * any positive value; a multiple of 32 keeps every 32-key chunk whole.
+ * num_blocks == 0 makes every sequence empty (O = 0, LSE = -inf).
+ * Sizes: num_blocks >= 0, block_size >= 1, max_blocks_per_seq >= 0,
+ * max_blocks_per_seq * block_size < 2^31, num_blocks * Hkv * block_size < 2^31;
+ * otherwise as for attn_decode.
+ */
+int attn_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                      const int32_t *block_table, const int32_t *seq_lens,
+                      void *o, float *lse, int B, int Hq, int Hkv,
+                      int num_blocks, int block_size, int max_blocks_per_seq,
+                      int d, float scale, int keys_per_split, int dtype,
+                      void *workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *attn_status_str(int status);
 

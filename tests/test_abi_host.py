@@ -23,7 +23,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert names == sorted(["attn_fwd", "attn_decode", "attn_decode_workspace_bytes", "attn_status_str"])
+    assert names == sorted(["attn_fwd", "attn_decode", "attn_decode_paged", "attn_decode_workspace_bytes",
+                            "attn_status_str"])
     lib = ctypes.CDLL(E.lib_path())
     for n in names:
         assert hasattr(lib, n), "libattn.so does not export %s" % n
@@ -124,3 +125,37 @@ def test_decode_workspace_bytes():
     # exactly the workspace that size reports is accepted, one byte less is not
     need = f(2, 8, 2, 512, 128)
     assert dec(ws_bytes=need - 1) == E.ATTN_ERR_WORKSPACE
+
+
+def pdec(q=P, kp=P, vp=P, bt=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, nb=16, bs=32, mb=8, d=128, scale=0.09, kps=0,
+         dtype=1, ws=P, ws_bytes=1 << 30):
+    return E.lib().attn_decode_paged(q, kp, vp, bt, sl, o, lse, B, Hq, Hkv, nb, bs, mb, d, scale, kps, dtype, ws,
+                                     ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nb=-1), E.ATTN_ERR_INVALID_ARG),
+    (dict(bs=0), E.ATTN_ERR_INVALID_ARG),
+    (dict(mb=-1), E.ATTN_ERR_INVALID_ARG),
+    (dict(bt=None), E.ATTN_ERR_INVALID_ARG),
+    (dict(bt=P + 2), E.ATTN_ERR_INVALID_ARG),
+    (dict(mb=1 << 20, bs=1 << 12), E.ATTN_ERR_UNSUPPORTED),     # max_blocks * block_size >= 2^31
+    (dict(nb=1 << 20, bs=1 << 10), E.ATTN_ERR_UNSUPPORTED),     # pool rows >= 2^31
+    (dict(Hq=6, Hkv=4), E.ATTN_ERR_INVALID_ARG),
+    (dict(dtype=0), E.ATTN_ERR_UNSUPPORTED),
+    (dict(d=96), E.ATTN_ERR_UNSUPPORTED),
+    (dict(kp=None), E.ATTN_ERR_INVALID_ARG),
+    (dict(ws=None), E.ATTN_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), E.ATTN_ERR_WORKSPACE),
+    (dict(B=0), E.ATTN_OK),
+])
+def test_decode_paged_validation(kw, status):
+    assert pdec(**kw) == status
+
+
+def test_decode_paged_workspace_is_the_contiguous_one():
+    """Sized like attn_decode with max_seq_len = max_blocks * block_size: one
+    byte less is refused (a sufficient size would launch, so it is not tried
+    here)."""
+    need = E.attn_decode_workspace_bytes(2, 8, 2, 8 * 32, 128)
+    assert pdec(ws_bytes=need - 1) == E.ATTN_ERR_WORKSPACE

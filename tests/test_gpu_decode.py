@@ -143,3 +143,91 @@ def test_workspace_reuse_and_explicit_buffer(orc):
     small = E.attn_decode_workspace_bytes(4, 32, 8, 512, 128)
     with pytest.raises(E.AttnError):
         E.attn_decode(dev(q), dev(kc), dev(vc), dev(sl), workspace=ws[: small - 16])
+
+
+# ---------------------------------------------------------------------------
+# Paged KV cache (attn_decode_paged)
+# ---------------------------------------------------------------------------
+def gpu_decode_paged(sl, q, kp, vp, bt, scale, keys_per_split=0):
+    o, lse = E.attn_decode_paged(dev(q), dev(kp), dev(vp), dev(bt), dev(sl.to(torch.int32)), scale=scale,
+                                 keys_per_split=keys_per_split)
+    torch.cuda.synchronize()
+    return I.to_f64(o), I.to_f64(lse)
+
+
+def _paged_parity(orc, sl, q, kp, vp, bt, scale, label, kps=0):
+    say("[paged] %s q%s pool%s table%s kps=%d L=%s" % (label, tuple(q.shape), tuple(kp.shape), tuple(bt.shape), kps,
+                                                       sl.tolist()[:8]))
+    o, lse = gpu_decode_paged(sl, q, kp, vp, bt, scale, kps)
+    o_ref, lse_ref = orc.decode_paged(I.to_f64(q), I.to_f64(kp), I.to_f64(vp), bt.numpy(), sl.numpy(), scale)
+    assert_close(label + " O", o, o_ref, TOL_O["bf16"])
+    assert_close(label + " LSE", lse, lse_ref, TOL_LSE)
+    return o, lse
+
+
+@pytest.mark.parametrize("bs", [16, 64, 256])
+def test_paged_kv_cache_workload(orc, bs):
+    """The KV-cache decode workload's shape (16 sequences, 32 query heads over
+    8 KV heads, d = 128, lengths uniform in [512, 4096]) in a shuffled pool."""
+    sl, q, kp, vp, bt = I.paged_decode_inputs(16, 32, 8, 128, bs, 4096 // bs, "bf16", seed=1104, spare_blocks=3)
+    _paged_parity(orc, sl, q, kp, vp, bt, 1 / np.sqrt(128), "C5 paged bs=%d" % bs)
+
+
+@pytest.mark.parametrize("bs,G,d,kps", [(32, 4, 128, 0), (48, 2, 64, 0), (1, 8, 128, 0), (7, 4, 64, 100),
+                                        (128, 16, 128, 1), (33, 24, 128, 0)])
+def test_paged_block_sizes_and_groups(orc, bs, G, d, kps):
+    Hkv = 2
+    sl, q, kp, vp, bt = I.paged_decode_inputs(5, G * Hkv, Hkv, d, bs, -(-700 // bs), "bf16", seed=1200 + bs + G,
+                                              lo=0, hi=700, spare_blocks=2)
+    _paged_parity(orc, sl, q, kp, vp, bt, 1 / np.sqrt(d), "bs=%d G=%d d=%d" % (bs, G, d), kps)
+
+
+def test_paged_equals_contiguous(orc):
+    """The same rows paged (identity table) and contiguous give the same
+    results within tolerance, and both match the oracle."""
+    sl, q, kc, vc = I.decode_inputs(6, 16, 4, 1024, 128, "bf16", seed=1300, lo=1, hi=1024)
+    bs = 64
+    mb = 1024 // bs
+    kp = kc.reshape(6, 4, mb, bs, 128).permute(0, 2, 1, 3, 4).reshape(6 * mb, 4, bs, 128).contiguous()
+    vp = vc.reshape(6, 4, mb, bs, 128).permute(0, 2, 1, 3, 4).reshape(6 * mb, 4, bs, 128).contiguous()
+    bt = torch.arange(6 * mb, dtype=torch.int32).reshape(6, mb)
+    op, lp = gpu_decode_paged(sl, q, kp, vp, bt, 0.088)
+    oc, lc = gpu_decode(sl, q, kc, vc, 0.088)
+    assert_close("paged vs contiguous O", op, oc, TOL_O["bf16"])
+    assert_close("paged vs contiguous LSE", lp, lc, 1e-5)
+    o_ref, l_ref = orc.decode(I.to_f64(q), I.to_f64(kc), I.to_f64(vc), sl.numpy(), 0.088)
+    assert_close("paged vs oracle O", op, o_ref, TOL_O["bf16"])
+
+
+def test_paged_shared_prefix_unused_blocks_and_clamping(orc):
+    """Sequences sharing prefix blocks; every block no valid row lives in is
+    poisoned with NaN (never read: bitwise equal results); table entries out
+    of range are clamped into the pool, as the oracle does."""
+    sl, q, kp, vp, bt = I.paged_decode_inputs(6, 8, 2, 128, 32, 20, "bf16", seed=1400, lo=100, hi=640,
+                                              spare_blocks=5)
+    bt[1, :3] = bt[0, :3]
+    bt[3, :2] = bt[0, :2]
+    o1, l1 = _paged_parity(orc, sl, q, kp, vp, bt, 0.088, "shared prefix")
+    used = set()
+    for b in range(6):
+        used.update(int(x) for x in bt[b, :(int(sl[b]) + 31) // 32].tolist())
+    kpp, vpp = kp.clone(), vp.clone()
+    for blk in range(kp.shape[0]):
+        if blk not in used:
+            kpp[blk] = float("nan")
+            vpp[blk] = float("nan")
+    o2, l2 = gpu_decode_paged(sl, q, kpp, vpp, bt, 0.088)
+    assert np.isfinite(o2).all()
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    bt2 = bt.clone()
+    bt2[2, 0] = -5
+    bt2[4, 1] = kp.shape[0] + 9
+    _paged_parity(orc, sl, q, kp, vp, bt2, 0.088, "clamped entries")
+
+
+def test_paged_empty_pool():
+    q = torch.randn(3, 8, 64).to(torch.bfloat16)
+    kp = torch.empty(0, 2, 32, 64, dtype=torch.bfloat16)
+    bt = torch.zeros(3, 4, dtype=torch.int32)
+    o, lse = gpu_decode_paged(torch.tensor([5, 0, 100], dtype=torch.int32), q, kp, kp.clone(), bt, 0.125)
+    assert (o == 0).all() and np.isneginf(lse).all()
