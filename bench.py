@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-paged]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-paged] [--no-rect]
 
 One step is one pass of the whole path over synthetic inputs already resident
 in device memory:
@@ -19,7 +19,9 @@ fraction from its average duration measured with HIP events on the stream the
 kernels run on.  `cpu_baseline` times the fp64 oracle on a bounded sample of the
 prefill rows on the host cores.  `decode_paged` times the decode workload
 against a paged cache (block table over a shuffled pool) on its own, after the
-timed steps.
+timed steps; `chunked_prefill` (a 2048-token chunk over 8192 cached tokens,
+causal bottom-right) and `cross_attention` (2048 queries over 4096 keys,
+non-causal) time attn_fwd on the two rectangular workloads the same way.
 """
 import argparse
 import json
@@ -50,6 +52,8 @@ def parse():
                     help="run one kernel only (for profiling runs)")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache decode measurement")
     ap.add_argument("--paged-block-size", type=int, default=64)
+    ap.add_argument("--no-rect", action="store_true",
+                    help="skip the chunked-prefill and cross-attention measurements")
     return ap.parse_args()
 
 
@@ -89,22 +93,47 @@ def paged_decode_line(E, A, I, dev, block_size, reps=4, steps=20, warmup=50):
         k_p, v_p = pools[i % reps]
         E.attn_decode_paged(q, k_p, v_p, bt, sl_d, scale=wd.scale, o=o, lse=lse, workspace=ws)
 
+    ms = timed_ms(call, steps, warmup)
+    by = A.decode_bytes(sl.tolist(), wd.Hq, wd.Hkv, wd.d, wd.dtype)
+    return {"value": round(by / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "frac_hbm": round(by / (ms * 1e-3) / 1e9 /
+            PEAK_HBM_GBS, 4), "avg_launch_ms": round(ms, 5), "block_size": block_size,
+            "sum_seq_len": int(sl.sum()), "bytes_per_launch": by,
+            "note": "same shape and lengths as the decode workload, rows in a shuffled pool of blocks"}
+
+
+def timed_ms(call, steps, warmup):
+    """Average duration of call() over `steps` launches, from HIP events on the
+    current stream, after `warmup` untimed ones."""
+    import torch
+
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
+    stream = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record(stream)
     for i in range(steps):
         call(i)
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(steps)) / steps
-    by = A.decode_bytes(sl.tolist(), wd.Hq, wd.Hkv, wd.d, wd.dtype)
-    return {"value": round(by / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "frac_hbm": round(by / (ms * 1e-3) / 1e9 /
-            PEAK_HBM_GBS, 4), "avg_launch_ms": round(ms, 5), "block_size": block_size,
-            "sum_seq_len": int(sl.sum()), "bytes_per_launch": by,
-            "note": "same shape and lengths as the decode workload, rows in a shuffled pool of blocks"}
+    return sum(ev[i].elapsed_time(ev[i + 1]) for i in range(steps)) / steps
+
+
+def rect_prefill_line(E, A, I, dev, name, steps=20, warmup=50):
+    """attn_fwd on a rectangular workload (Nq != Nk), timed on its own."""
+    import torch
+
+    w = I.WORKLOADS[name]
+    q, k, v = (t.to(dev) for t in I.workload_inputs(name))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    ms = timed_ms(lambda i: E.attn_fwd(q, k, v, scale=w.scale, causal=w.causal, o=o, lse=lse), steps, warmup)
+    fl = A.prefill_flops(w.B, w.Hq, w.Nq, w.Nkv, w.d, w.causal)
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "avg_launch_ms": round(ms, 5), "flops_per_launch": fl,
+            "shape": {"B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nkv, "d": w.d,
+                      "causal": w.causal}, "note": w.note}
 
 
 def cpu_baseline(q, k, v, w, target_s):
@@ -283,6 +312,9 @@ def main():
         }
     if run_d and not args.no_paged:
         out["decode_paged"] = paged_decode_line(E, A, I, dev, args.paged_block_size)
+    if run_p and not args.no_rect:
+        out["chunked_prefill"] = rect_prefill_line(E, A, I, dev, "X1")
+        out["cross_attention"] = rect_prefill_line(E, A, I, dev, "X2")
     if not args.no_cpu_baseline and run_p:
         out["cpu_baseline"] = cpu_baseline(q_cpu, k_cpu, v_cpu, wp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -29,10 +29,19 @@ class Prefill:
     causal: bool
     seed: int
     note: str = ""
+    Nk: int = 0  # key/value length; 0 = N (self-attention)
 
     @property
     def scale(self) -> float:
         return 1.0 / (self.d ** 0.5)
+
+    @property
+    def Nq(self) -> int:
+        return self.N
+
+    @property
+    def Nkv(self) -> int:
+        return self.Nk if self.Nk > 0 else self.N
 
 
 @dataclass(frozen=True)
@@ -72,6 +81,11 @@ WORKLOADS = {
                   "GQA prefill, 64 query heads over 8 KV heads, one 70B-class layer"),
     "C5": Decode("C5", 16, 32, 8, 4096, 128, "bf16", 512, 4096, 1004,
                  "KV-cache decode, 16 sequences, 32 Q heads over 8 KV heads"),
+    "X1": Prefill("X1", 1, 64, 8, 2048, 128, "bf16", True, 1005,
+                  "chunked prefill: a 2048-token chunk attending causally (bottom-right) to 8192 "
+                  "cached tokens plus itself, on the GQA layer's heads", Nk=10240),
+    "X2": Prefill("X2", 4, 16, 16, 2048, 128, "bf16", False, 1006,
+                  "cross-attention: 2048 decoder queries over 4096 encoder keys, non-causal", Nk=4096),
 }
 
 
@@ -138,7 +152,7 @@ def workload_inputs(name: str, seed_offset: int = 0):
     """Inputs of a named workload (prefill: (q,k,v); decode: (seq_lens,q,kc,vc))."""
     w = WORKLOADS[name]
     if isinstance(w, Prefill):
-        return prefill_inputs(w.B, w.Hq, w.Hkv, w.N, w.N, w.d, w.dtype, w.seed + seed_offset)
+        return prefill_inputs(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.d, w.dtype, w.seed + seed_offset)
     return decode_inputs(w.B, w.Hq, w.Hkv, w.Lmax, w.d, w.dtype, w.seed + seed_offset, w.lo, w.hi)
 
 

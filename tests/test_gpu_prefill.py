@@ -27,7 +27,7 @@ def test_workload_full_parity(orc, name, causal):
     _full_parity(orc, q, k, v, w.scale, causal, w.dtype, name)
 
 
-@pytest.mark.parametrize("name", ["C3a'", "C3b", "C4"])
+@pytest.mark.parametrize("name", ["C3a'", "C3b", "C4", "X1", "X2"])
 def test_workload_sampled_parity(orc, name):
     """Full-size workloads in the launch configuration the benchmark times,
     compared on sampled rows (every head's first and last row, tile edges and
@@ -37,7 +37,7 @@ def test_workload_sampled_parity(orc, name):
     say("[prefill] %s full size q%s k%s" % (name, tuple(q.shape), tuple(k.shape)))
     o, lse = E.attn_fwd(dev(q), dev(k), dev(v), scale=w.scale, causal=w.causal)
     torch.cuda.synchronize()
-    rows = sample_rows(w.B, w.Hq, w.N, 768, seed=w.seed)
+    rows = sample_rows(w.B, w.Hq, w.Nq, 768, seed=w.seed)
     o_ref, lse_ref = orc.attn_rows(I.to_f64(q), I.to_f64(k), I.to_f64(v), w.scale, w.causal, rows)
     og = o[rows[:, 0], rows[:, 1], rows[:, 2]]
     lg = lse[rows[:, 0], rows[:, 1], rows[:, 2]]
