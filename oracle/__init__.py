@@ -12,7 +12,8 @@ passage each step follows, is documented at the top of ``oracle.c``:
     s_ij = scale * q_i . k_j ;  a_ij = softmax_j(s_ij) over visible j ;
     o_i = sum_j a_ij v_j ;      lse_i = ln sum_j exp(s_ij)
 
-with bottom-right causal alignment and contiguous GQA groups.
+with bottom-right causal alignment and contiguous GQA groups, and the
+gradients dq, dk, dv of that definition for an upstream gradient do of o.
 
 Every function takes float64 arrays.  Inputs that the GPU sees as bf16 or fp32
 must be widened to float64 from exactly the stored values before the call.
@@ -40,6 +41,12 @@ def _bind(path):
     lib.oracle_decode.argtypes = [_dp, _dp, _dp, _ip, _dp, _dp] + [c_int] * 5 + [c_double, c_int]
     lib.oracle_decode_paged.argtypes = [_dp, _dp, _dp, _ip, _ip, _dp, _dp] + [c_int] * 7 + [c_double, c_int]
     lib.oracle_decode.restype = c_int
+    lib.oracle_decode_paged.restype = c_int
+    lib.oracle_attn_bwd.argtypes = [_dp] * 7 + [c_int] * 6 + [c_double, c_int, c_int]
+    lib.oracle_attn_bwd.restype = c_int
+    lib.oracle_attn_bwd_rows.argtypes = ([_dp] * 4 + [_ip, c_long, _ip, c_long] + [_dp] * 3 + [c_int] * 6 +
+                                         [c_double, c_int, c_int])
+    lib.oracle_attn_bwd_rows.restype = c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = c_int
     return lib
@@ -124,6 +131,50 @@ class Oracle:
         if rc:
             raise RuntimeError("oracle_blockwise failed")
         return o, lse
+
+    def attn_bwd(self, q, k, v, do, scale, causal=False, nthreads=0):
+        """Gradients of the direct definition for the upstream gradient do
+        [B,Hq,Nq,d] of o.  Returns (dq [B,Hq,Nq,d], dk [B,Hkv,Nk,d],
+        dv [B,Hkv,Nk,d])."""
+        B, Hq, Hkv, Nq, Nk, d = _shapes(q, k, v)
+        if tuple(do.shape) != (B, Hq, Nq, d):
+            raise ValueError("do must have q's shape")
+        q, qp = _f64(q)
+        k, kp = _f64(k)
+        v, vp = _f64(v)
+        do, dop = _f64(do)
+        dq = np.zeros((B, Hq, Nq, d))
+        dk = np.zeros((B, Hkv, Nk, d))
+        dv = np.zeros((B, Hkv, Nk, d))
+        rc = self.lib.oracle_attn_bwd(qp, kp, vp, dop, dq.ctypes.data_as(_dp), dk.ctypes.data_as(_dp),
+                                      dv.ctypes.data_as(_dp), B, Hq, Hkv, Nq, Nk, d, float(scale),
+                                      int(bool(causal)), int(nthreads))
+        if rc:
+            raise RuntimeError("oracle_attn_bwd failed")
+        return dq, dk, dv
+
+    def attn_bwd_rows(self, q, k, v, do, scale, causal, qrows, krows, nthreads=0):
+        """Selected gradient rows: dq at qrows (int [n,3] of b, h, i) and dk, dv
+        at krows (int [m,3] of b, hk, j).  Returns (dq [n,d], dk [m,d], dv [m,d])."""
+        B, Hq, Hkv, Nq, Nk, d = _shapes(q, k, v)
+        if tuple(do.shape) != (B, Hq, Nq, d):
+            raise ValueError("do must have q's shape")
+        q, qp = _f64(q)
+        k, kp = _f64(k)
+        v, vp = _f64(v)
+        do, dop = _f64(do)
+        qr = np.ascontiguousarray(qrows, dtype=np.int32).reshape(-1, 3)
+        kr = np.ascontiguousarray(krows, dtype=np.int32).reshape(-1, 3)
+        dq = np.zeros((qr.shape[0], d))
+        dk = np.zeros((kr.shape[0], d))
+        dv = np.zeros((kr.shape[0], d))
+        rc = self.lib.oracle_attn_bwd_rows(qp, kp, vp, dop, qr.ctypes.data_as(_ip), qr.shape[0],
+                                           kr.ctypes.data_as(_ip), kr.shape[0], dq.ctypes.data_as(_dp),
+                                           dk.ctypes.data_as(_dp), dv.ctypes.data_as(_dp), B, Hq, Hkv, Nq, Nk,
+                                           d, float(scale), int(bool(causal)), int(nthreads))
+        if rc:
+            raise RuntimeError("oracle_attn_bwd_rows failed")
+        return dq, dk, dv
 
     def decode(self, q, k_cache, v_cache, seq_lens, scale, nthreads=0):
         """One-token decode.  q [B,Hq,d], caches [B,Hkv,Lmax,d], seq_lens [B].
@@ -214,3 +265,11 @@ def decode(*a, **kw):
 
 def decode_paged(*a, **kw):
     return default().decode_paged(*a, **kw)
+
+
+def attn_bwd(*a, **kw):
+    return default().attn_bwd(*a, **kw)
+
+
+def attn_bwd_rows(*a, **kw):
+    return default().attn_bwd_rows(*a, **kw)

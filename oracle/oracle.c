@@ -14,6 +14,9 @@
  *   o_i   = sum_{j visible} a_ij v_j
  *   lse_i = m_i + ln(sum_{j visible} exp(s_ij - m_i))     (natural log)
  *
+ * and, for the backward pass, the chain-rule gradients dq, dk, dv of that
+ * definition for an upstream gradient do of o (see oracle_attn_bwd).
+ *
  * Pages followed (cited by title and section):
  *   [R]  "Transformer 架构的数学与计算深度解析：注意力机制的详尽研究报告"
  *        (menggq.pages.dev): sec. 2.2 (scores as dot products q_i.k_j),
@@ -42,7 +45,7 @@
  *
  * Layouts: every tensor is contiguous, row-major, fp64:
  *   q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d], o [B,Hq,Nq,d], lse [B,Hq,Nq],
- *   weights [B,Hq,Nq,Nk].  Decode: q [B,Hq,d], caches [B,Hkv,Lmax,d],
+ *   weights [B,Hq,Nq,Nk]; do/dq as q, dk/dv as k.  Decode: q [B,Hq,d], caches [B,Hkv,Lmax,d],
  *   seq_lens int32 [B], o [B,Hq,d], lse [B,Hq].
  *
  * Every entry point returns 0 on success, -1 on an invalid argument.
@@ -417,5 +420,257 @@ int oracle_decode(const double *q, const double *kc, const double *vc,
         }
         free(s);
     }
+    return bad ? -1 : 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Backward pass (gradients of the forward definition above).
+ *
+ * The pages state that training needs the gradients of attention ([R]
+ * sec. 3.3: the standard implementation keeps the N x N matrix for the
+ * backward pass), that FlashAttention recomputes instead of storing it
+ * ("Transformer 深度进阶" [M], the FlashAttention section: recomputation adds
+ * FLOPs but cuts memory traffic), and that an exact tiled kernel is checked by
+ * comparing outputs AND gradients with a higher-precision reference ([IO],
+ * the evaluation protocol).  They print no gradient formula.  The oracle
+ * therefore takes the derivative of the forward definition by the chain rule,
+ * for an upstream gradient dO of the output:
+ *
+ *   dv_j  = sum_i a_ij do_i                       (o_i = sum_j a_ij v_j)
+ *   dp_ij = do_i . v_j                            (dL/da_ij)
+ *   ds_ij = a_ij (dp_ij - sum_k a_ik dp_ik)       (softmax Jacobian)
+ *   dq_i  = scale * sum_j ds_ij k_j               (s_ij = scale q_i.k_j)
+ *   dk_j  = scale * sum_i ds_ij q_i
+ *
+ * with masked pairs contributing nothing, and for GQA the sum over every
+ * query head of the group into the shared K/V head's dk, dv.  A finite-
+ * difference test of the forward pins these formulas.
+ * ------------------------------------------------------------------------ */
+
+/* Gradient contributions of one query row.  qrow, dorow: d values; K, V: the
+ * nvis visible rows; a, dp: scratch of nvis doubles; dqrow receives dq_i;
+ * dK, dV (row stride d) accumulate this row's share of dk_j, dv_j. */
+static void bwd_row(const double *qrow, const double *dorow, const double *K,
+                    const double *V, long nvis, long d, double scale, double *a,
+                    double *dp, double *orow_scratch, double *dqrow, double *dK,
+                    double *dV)
+{
+    long j, c;
+    double lse;
+    for (c = 0; c < d; ++c)
+        dqrow[c] = 0.0;
+    if (nvis == 0)
+        return;
+    direct_row(qrow, K, V, nvis, d, scale, dp, orow_scratch, &lse, a); /* a_ij */
+    double D = 0.0;
+    for (j = 0; j < nvis; ++j) {
+        double acc = 0.0;
+        for (c = 0; c < d; ++c)
+            acc += dorow[c] * V[j * d + c];
+        dp[j] = acc;
+        D += a[j] * acc;
+    }
+    for (j = 0; j < nvis; ++j) {
+        double ds = a[j] * (dp[j] - D);
+        for (c = 0; c < d; ++c) {
+            dqrow[c] += scale * ds * K[j * d + c];
+            dK[j * d + c] += scale * ds * qrow[c];
+            dV[j * d + c] += a[j] * dorow[c];
+        }
+    }
+}
+
+/* Full backward: dq [B,Hq,Nq,d], dk/dv [B,Hkv,Nk,d] (layouts as the forward),
+ * from q, k, v and the upstream gradient do_ [B,Hq,Nq,d].  One (b, KV head)
+ * per task, so each task owns its dk/dv rows. */
+int oracle_attn_bwd(const double *q, const double *k, const double *v,
+                    const double *do_, double *dq, double *dk, double *dv,
+                    int B, int Hq, int Hkv, int Nq, int Nk, int d, double scale,
+                    int causal, int nthreads)
+{
+    if (check_shape(B, Hq, Hkv, Nq, Nk, d))
+        return -1;
+    set_threads(nthreads);
+    const long G = Hq / Hkv;
+    const long groups = (long)B * Hkv;
+    int bad = 0;
+#pragma omp parallel
+    {
+        const size_t n = (size_t)(Nk > 0 ? Nk : 1);
+        double *a = (double *)malloc(sizeof(double) * n);
+        double *dp = (double *)malloc(sizeof(double) * n);
+        double *orow = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!a || !dp || !orow) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long t = 0; t < groups; ++t) {
+            if (!a || !dp || !orow)
+                continue;
+            long b = t / Hkv, hk = t % Hkv;
+            const long kv0 = ((b * Hkv + hk) * (long)Nk) * d;
+            double *dK = dk + kv0, *dV = dv + kv0;
+            memset(dK, 0, sizeof(double) * (size_t)Nk * d);
+            memset(dV, 0, sizeof(double) * (size_t)Nk * d);
+            for (long h = hk * G; h < (hk + 1) * G; ++h) { /* [E] sec. 2.3 */
+                for (long i = 0; i < Nq; ++i) {
+                    const long r = ((b * Hq + h) * (long)Nq + i) * d;
+                    bwd_row(q + r, do_ + r, k + kv0, v + kv0,
+                            visible_keys(i, Nq, Nk, causal), d, scale, a, dp,
+                            orow, dq + r, dK, dV);
+                }
+            }
+        }
+        free(a);
+        free(dp);
+        free(orow);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Selected gradient rows of the same definition, for sizes where the full
+ * backward is too slow: dq for the nq query rows qrows (triples b, h, i) and
+ * dk, dv for the nk key rows krows (triples b, hk, j).
+ *
+ * A key row's gradient needs, for every query row i of its group that sees
+ * it, the weight a_ij and D_i = sum_k a_ik dp_ik; with lse_i the log of the
+ * row's denominator, a_ij = exp(s_ij - lse_i) ([R] sec. 2.4 written with the
+ * log-sum-exp).  Both statistics come from the direct definition of each such
+ * row, then the key row sums its terms over i in index order. */
+int oracle_attn_bwd_rows(const double *q, const double *k, const double *v,
+                         const double *do_, const int32_t *qrows, long nq,
+                         const int32_t *krows, long nk, double *dq_out,
+                         double *dk_out, double *dv_out, int B, int Hq, int Hkv,
+                         int Nq, int Nk, int d, double scale, int causal,
+                         int nthreads)
+{
+    if (check_shape(B, Hq, Hkv, Nq, Nk, d))
+        return -1;
+    for (long t = 0; t < nq; ++t)
+        if (qrows[3 * t] < 0 || qrows[3 * t] >= B || qrows[3 * t + 1] < 0 ||
+            qrows[3 * t + 1] >= Hq || qrows[3 * t + 2] < 0 || qrows[3 * t + 2] >= Nq)
+            return -1;
+    for (long t = 0; t < nk; ++t)
+        if (krows[3 * t] < 0 || krows[3 * t] >= B || krows[3 * t + 1] < 0 ||
+            krows[3 * t + 1] >= Hkv || krows[3 * t + 2] < 0 || krows[3 * t + 2] >= Nk)
+            return -1;
+    set_threads(nthreads);
+    const long G = Hq / Hkv;
+    int bad = 0;
+
+    /* dq rows: each is the dq of bwd_row, with the dk/dv shares discarded */
+#pragma omp parallel
+    {
+        const size_t n = (size_t)(Nk > 0 ? Nk : 1);
+        double *a = (double *)malloc(sizeof(double) * n);
+        double *dp = (double *)malloc(sizeof(double) * n);
+        double *orow = (double *)malloc(sizeof(double) * (size_t)d);
+        double *sink = (double *)calloc(n * (size_t)d * 2, sizeof(double));
+        if (!a || !dp || !orow || !sink) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long t = 0; t < nq; ++t) {
+            if (!a || !dp || !orow || !sink)
+                continue;
+            long b = qrows[3 * t], h = qrows[3 * t + 1], i = qrows[3 * t + 2];
+            long hk = h / G;
+            const long r = ((b * Hq + h) * (long)Nq + i) * d;
+            const long kv0 = ((b * Hkv + hk) * (long)Nk) * d;
+            bwd_row(q + r, do_ + r, k + kv0, v + kv0, visible_keys(i, Nq, Nk, causal),
+                    d, scale, a, dp, orow, dq_out + t * d, sink, sink + n * (size_t)d);
+        }
+        free(a);
+        free(dp);
+        free(orow);
+        free(sink);
+    }
+    if (bad || nk == 0)
+        return bad ? -1 : 0;
+
+    /* statistics (lse_i, D_i) of every row of every group that a key row names */
+    char *need = (char *)calloc((size_t)B * Hkv, 1);
+    double *lse = (double *)malloc(sizeof(double) * (size_t)B * Hq * (Nq > 0 ? Nq : 1));
+    double *Dst = (double *)malloc(sizeof(double) * (size_t)B * Hq * (Nq > 0 ? Nq : 1));
+    if (!need || !lse || !Dst) {
+        free(need);
+        free(lse);
+        free(Dst);
+        return -1;
+    }
+    for (long t = 0; t < nk; ++t)
+        need[krows[3 * t] * (long)Hkv + krows[3 * t + 1]] = 1;
+    const long rows = (long)B * Hq * Nq;
+#pragma omp parallel
+    {
+        const size_t n = (size_t)(Nk > 0 ? Nk : 1);
+        double *a = (double *)malloc(sizeof(double) * n);
+        double *sc = (double *)malloc(sizeof(double) * n);
+        double *orow = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!a || !sc || !orow) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (long r = 0; r < rows; ++r) {
+            if (!a || !sc || !orow)
+                continue;
+            long i = r % Nq, h = (r / Nq) % Hq, b = r / ((long)Nq * Hq), hk = h / G;
+            if (!need[b * Hkv + hk])
+                continue;
+            const long kv0 = ((b * Hkv + hk) * (long)Nk) * d;
+            long nvis = visible_keys(i, Nq, Nk, causal);
+            direct_row(q + r * d, k + kv0, v + kv0, nvis, d, scale, sc, orow, lse + r, a);
+            double D = 0.0;
+            for (long j = 0; j < nvis; ++j) {
+                double acc = 0.0;
+                for (long c = 0; c < d; ++c)
+                    acc += do_[r * d + c] * v[kv0 + j * d + c];
+                D += a[j] * acc;
+            }
+            Dst[r] = D;
+        }
+        free(a);
+        free(sc);
+        free(orow);
+    }
+    /* dk, dv rows */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long t = 0; t < nk; ++t) {
+        if (bad)
+            continue;
+        long b = krows[3 * t], hk = krows[3 * t + 1], j = krows[3 * t + 2];
+        const double *kj = k + (((b * Hkv + hk) * (long)Nk) + j) * d;
+        const double *vj = v + (((b * Hkv + hk) * (long)Nk) + j) * d;
+        double *dkr = dk_out + t * d, *dvr = dv_out + t * d;
+        for (long c = 0; c < d; ++c) {
+            dkr[c] = 0.0;
+            dvr[c] = 0.0;
+        }
+        for (long h = hk * G; h < (hk + 1) * G; ++h) {
+            for (long i = 0; i < Nq; ++i) {
+                if (j >= visible_keys(i, Nq, Nk, causal))
+                    continue;
+                const long r = (b * Hq + h) * (long)Nq + i;
+                const double *qi = q + r * d, *doi = do_ + r * d;
+                double s = 0.0, dpv = 0.0;
+                for (long c = 0; c < d; ++c) {
+                    s += qi[c] * kj[c];
+                    dpv += doi[c] * vj[c];
+                }
+                const double aij = exp(scale * s - lse[r]);
+                const double ds = aij * (dpv - Dst[r]);
+                for (long c = 0; c < d; ++c) {
+                    dkr[c] += scale * ds * qi[c];
+                    dvr[c] += aij * doi[c];
+                }
+            }
+        }
+    }
+    free(need);
+    free(lse);
+    free(Dst);
     return bad ? -1 : 0;
 }

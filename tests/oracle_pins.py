@@ -20,6 +20,9 @@ Pages (cited by title and section):
   [E]  pwwt.cn engineering blog: sec. 2.3 (GQA: a group of query heads shares
        one K/V head), sec. 5.1 (attention is order-insensitive: shuffling the
        sequence only shuffles the output).
+  [M]  "Transformer 深度进阶：从矩阵视角到 FlashAttention 工程优化": the
+       FlashAttention section (the backward pass recomputes instead of storing
+       the score matrix).
 """
 from decimal import Decimal, getcontext
 
@@ -407,6 +410,148 @@ def pin_rows_entry_matches_full(orc):
         _close(lr, lse[rows[:, 0], rows[:, 1], rows[:, 2]], 0.0, "attn_rows lse")
 
 
+# ---------------------------------------------------------------------------
+# 4. backward pass: gradients of the forward definition ([R] sec. 3.3 and
+#    [M]'s FlashAttention section: training needs them; [IO], the evaluation
+#    protocol: compare gradients with a higher-precision reference).
+# ---------------------------------------------------------------------------
+def _bottom_right_mask(Nq, Nk):
+    """True where key j is hidden from query row i (j > i + Nk - Nq)."""
+    i = torch.arange(Nq).unsqueeze(1)
+    j = torch.arange(Nk).unsqueeze(0)
+    return j > i + (Nk - Nq)
+
+
+def pin_bwd_finite_differences(orc):
+    """Central differences of the scalar L = sum(do * o(q, k, v)), with o from
+    the oracle's forward (itself pinned above), against every element of
+    dq, dk, dv.  Independent of the gradient formulas: a dropped term, a sign,
+    a transposed operand, a missing scale or a GQA head summed wrongly each
+    moves some element by far more than the O(h^2) difference error."""
+    rng = _rng(20)
+    cases = [
+        (1, 2, 1, 5, 7, 3, True),    # GQA, chunked (bottom-right)
+        (1, 2, 2, 6, 6, 4, False),
+        (2, 3, 1, 4, 4, 2, True),    # MQA, square causal
+        (1, 2, 1, 6, 3, 3, False),   # cross-attention, Nq > Nk
+    ]
+    h = 1e-5
+    for (B, Hq, Hkv, Nq, Nk, d, causal) in cases:
+        q = _randn(rng, B, Hq, Nq, d)
+        k = _randn(rng, B, Hkv, Nk, d)
+        v = _randn(rng, B, Hkv, Nk, d)
+        do = _randn(rng, B, Hq, Nq, d)
+        scale = 0.7
+        dq, dk, dv = orc.attn_bwd(q, k, v, do, scale, causal)
+
+        def loss(q_, k_, v_):
+            return float(np.sum(do * orc.attn(q_, k_, v_, scale, causal)[0]))
+
+        for name, x, g in (("dq", q, dq), ("dk", k, dk), ("dv", v, dv)):
+            fd = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                xp = x.copy()
+                xm = x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = [q, k, v]
+                args_m = [q, k, v]
+                slot = {"dq": 0, "dk": 1, "dv": 2}[name]
+                args_p[slot] = xp
+                args_m[slot] = xm
+                fd[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            _close(g, fd, 1e-7, "%s vs finite differences %s" % (name, (B, Hq, Hkv, Nq, Nk, d, causal)))
+
+
+def pin_bwd_torch_autograd(orc):
+    """Library special case: torch autograd through the fp64 CPU
+    scaled_dot_product_attention, with an explicit bottom-right mask and the
+    K/V heads repeated for their query heads (autograd sums the repeats)."""
+    rng = _rng(21)
+    cases = [
+        (2, 4, 2, 33, 47, 16, True),
+        (2, 4, 2, 33, 47, 16, False),
+        (1, 6, 1, 40, 40, 8, True),
+        (1, 2, 2, 64, 128, 32, True),
+    ]
+    for (B, Hq, Hkv, Nq, Nk, d, causal) in cases:
+        q = _randn(rng, B, Hq, Nq, d)
+        k = _randn(rng, B, Hkv, Nk, d)
+        v = _randn(rng, B, Hkv, Nk, d)
+        do = _randn(rng, B, Hq, Nq, d)
+        scale = 1.0 / np.sqrt(d)
+        tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+        G = Hq // Hkv
+        mask = ~_bottom_right_mask(Nq, Nk) if causal else None
+        o = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk.repeat_interleave(G, dim=1), tv.repeat_interleave(G, dim=1), attn_mask=mask, scale=scale)
+        o.backward(torch.from_numpy(do))
+        dq, dk, dv = orc.attn_bwd(q, k, v, do, scale, causal)
+        tag = (B, Hq, Hkv, Nq, Nk, d, causal)
+        _close(dq, tq.grad.numpy(), 1e-10, "dq vs torch autograd %s" % (tag,))
+        _close(dk, tk.grad.numpy(), 1e-10, "dk vs torch autograd %s" % (tag,))
+        _close(dv, tv.grad.numpy(), 1e-10, "dv vs torch autograd %s" % (tag,))
+
+
+def pin_bwd_closed_forms(orc):
+    """Facts of the definition that hold for any inputs:
+      * each row of weights sums to one, so sum_j dv_j = sum of do_i over the
+        group's rows that see some key, and the softmax Jacobian's rows sum to
+        zero, so sum_j dk_j = 0 ([R] sec. 2.4);
+      * with one key the weights are constant (= 1): dq = 0, dk = 0 and
+        dv_0 = sum of every do_i of the group;
+      * square causal row 0 sees only key 0 ([R] sec. 4.1): its dq is 0;
+      * the gradients are linear in do, and do = 0 gives zeros."""
+    rng = _rng(22)
+    B, Hq, Hkv, d = 2, 6, 2, 5
+    G = Hq // Hkv
+    for (Nq, Nk, causal) in ((9, 9, True), (9, 9, False), (4, 11, True), (7, 3, False)):
+        q = _randn(rng, B, Hq, Nq, d)
+        k = _randn(rng, B, Hkv, Nk, d)
+        v = _randn(rng, B, Hkv, Nk, d)
+        do = _randn(rng, B, Hq, Nq, d)
+        dq, dk, dv = orc.attn_bwd(q, k, v, do, 0.4, causal)
+        do_g = do.reshape(B, Hkv, G, Nq, d).sum(axis=(2, 3))
+        _close(dv.sum(axis=2), do_g, 1e-12, "sum_j dv_j = sum_i do_i")
+        _close(dk.sum(axis=2), np.zeros((B, Hkv, d)), 1e-12, "sum_j dk_j = 0")
+        if causal and Nq == Nk:
+            _close(dq[:, :, 0], np.zeros((B, Hq, d)), 0.0, "causal row 0: dq = 0")
+        dq2, dk2, dv2 = orc.attn_bwd(q, k, v, -2.5 * do, 0.4, causal)
+        _close(dq2, -2.5 * dq, 1e-12, "dq linear in do")
+        _close(dk2, -2.5 * dk, 1e-12, "dk linear in do")
+        _close(dv2, -2.5 * dv, 1e-12, "dv linear in do")
+        z = orc.attn_bwd(q, k, v, np.zeros_like(do), 0.4, causal)
+        for t in z:
+            _close(t, np.zeros_like(t), 0.0, "do = 0")
+    q = _randn(rng, B, Hq, 5, d)
+    k = _randn(rng, B, Hkv, 1, d)
+    v = _randn(rng, B, Hkv, 1, d)
+    do = _randn(rng, B, Hq, 5, d)
+    dq, dk, dv = orc.attn_bwd(q, k, v, do, 0.4, False)
+    _close(dq, np.zeros_like(dq), 0.0, "one key: dq = 0")
+    _close(dk, np.zeros_like(dk), 1e-12, "one key: dk = 0")
+    _close(dv[:, :, 0], do.reshape(B, Hkv, G, 5, d).sum(axis=(2, 3)), 1e-12, "one key: dv = sum do")
+
+
+def pin_bwd_rows_match_full(orc):
+    """The selected-rows entry (weights from the log-sum-exp) equals the full
+    backward on the rows it names."""
+    rng = _rng(23)
+    B, Hq, Hkv, d = 2, 4, 2, 6
+    for (Nq, Nk, causal) in ((20, 20, True), (13, 29, True), (17, 9, False)):
+        q = _randn(rng, B, Hq, Nq, d)
+        k = _randn(rng, B, Hkv, Nk, d)
+        v = _randn(rng, B, Hkv, Nk, d)
+        do = _randn(rng, B, Hq, Nq, d)
+        dq, dk, dv = orc.attn_bwd(q, k, v, do, 0.5, causal)
+        qr = np.array([[0, 0, 0], [1, 3, Nq - 1], [0, 2, Nq // 2], [1, 1, 3]], dtype=np.int32)
+        kr = np.array([[0, 0, 0], [1, 1, Nk - 1], [0, 1, Nk // 2], [1, 0, 2]], dtype=np.int32)
+        gq, gk, gv = orc.attn_bwd_rows(q, k, v, do, 0.5, causal, qr, kr)
+        _close(gq, dq[qr[:, 0], qr[:, 1], qr[:, 2]], 1e-12, "bwd rows dq")
+        _close(gk, dk[kr[:, 0], kr[:, 1], kr[:, 2]], 1e-12, "bwd rows dk")
+        _close(gv, dv[kr[:, 0], kr[:, 1], kr[:, 2]], 1e-12, "bwd rows dv")
+
+
 ALL_PINS = [
     pin_decimal_bruteforce,
     pin_torch_sdpa,
@@ -423,4 +568,8 @@ ALL_PINS = [
     pin_paged_decode,
     pin_blockwise_equals_direct,
     pin_rows_entry_matches_full,
+    pin_bwd_finite_differences,
+    pin_bwd_torch_autograd,
+    pin_bwd_closed_forms,
+    pin_bwd_rows_match_full,
 ]

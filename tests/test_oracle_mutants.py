@@ -38,6 +38,19 @@ MUTANTS = [
     ("paged_head_major", [("const long src = ((blk * Hkv + hk)", "const long src = ((hk * num_blocks + blk)")]),
     ("paged_block_index", [("block_table[b * (long)max_blocks + j / bs]", "block_table[b * (long)max_blocks + j % max_blocks]")]),
     ("paged_no_entry_clamp", [("if (blk > num_blocks - 1)\n                    blk = num_blocks - 1;", "")]),
+    ("bwd_drop_row_term", [("double ds = a[j] * (dp[j] - D);", "double ds = a[j] * dp[j];")]),
+    ("bwd_dk_no_scale", [("dK[j * d + c] += scale * ds * qrow[c];", "dK[j * d + c] += ds * qrow[c];")]),
+    ("bwd_dv_uses_ds", [("dV[j * d + c] += a[j] * dorow[c];", "dV[j * d + c] += ds * dorow[c];")]),
+    ("bwd_dp_uses_k", [("acc += dorow[c] * V[j * d + c];", "acc += dorow[c] * K[j * d + c];")]),
+    ("bwd_dq_uses_v", [("dqrow[c] += scale * ds * K[j * d + c];", "dqrow[c] += scale * ds * V[j * d + c];")]),
+    ("bwd_dq_sign", [("dqrow[c] += scale * ds * K[j * d + c];", "dqrow[c] -= scale * ds * K[j * d + c];")]),
+    ("bwd_first_head_only", [("for (long h = hk * G; h < (hk + 1) * G; ++h) { /* [E] sec. 2.3 */",
+                              "for (long h = hk * G; h < hk * G + 1; ++h) {")]),
+    ("bwd_unmasked", [("visible_keys(i, Nq, Nk, causal), d, scale, a, dp,", "Nk, d, scale, a, dp,")]),
+    ("bwd_rows_weight_without_lse", [("const double aij = exp(scale * s - lse[r]);",
+                                      "const double aij = exp(scale * s);")]),
+    ("bwd_rows_no_row_term", [("Dst[r] = D;", "Dst[r] = 0.0;")]),
+    ("bwd_rows_sees_future", [("if (j >= visible_keys(i, Nq, Nk, causal))", "if (j >= Nk)")]),
 ]
 
 
