@@ -13,6 +13,9 @@ Functions carry the names of the C entry points:
     attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, o=None,
                       lse=None, workspace=None, keys_per_split=0, return_lse=True)
     attn_decode_workspace_bytes(B, Hq, Hkv, max_seq_len, d, keys_per_split=0)
+    attn_bwd(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None, dv=None,
+             workspace=None)
+    attn_bwd_workspace_bytes(B, Hq, Nq)
     attn_status_str(status)
 
 There is no fallback: if libattn.so is missing or a call fails, an exception is
@@ -27,6 +30,8 @@ from ._binding import (  # noqa: F401
     ATTN_F32,
     ATTN_OK,
     AttnError,
+    attn_bwd,
+    attn_bwd_workspace_bytes,
     attn_decode,
     attn_decode_paged,
     attn_decode_workspace_bytes,
@@ -41,6 +46,8 @@ __all__ = [
     "attn_decode",
     "attn_decode_paged",
     "attn_decode_workspace_bytes",
+    "attn_bwd",
+    "attn_bwd_workspace_bytes",
     "attn_status_str",
     "AttnError",
 ]

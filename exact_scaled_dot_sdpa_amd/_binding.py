@@ -41,6 +41,10 @@ def lib():
     L.attn_decode.restype = i
     L.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp, sz, vp]
     L.attn_decode_paged.restype = i
+    L.attn_bwd_workspace_bytes.argtypes = [i, i, i]
+    L.attn_bwd_workspace_bytes.restype = sz
+    L.attn_bwd.argtypes = [vp] * 9 + [i] * 6 + [f, i, i, vp, sz, vp]
+    L.attn_bwd.restype = i
     L.attn_status_str.argtypes = [i]
     L.attn_status_str.restype = ctypes.c_char_p
     _lib = L
@@ -115,6 +119,48 @@ def attn_fwd(q, k, v, scale=None, causal=False, o=None, lse=None, return_lse=Tru
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd")
     return (o, lse) if return_lse else o
+
+
+def attn_bwd_workspace_bytes(B, Hq, Nq) -> int:
+    return int(lib().attn_bwd_workspace_bytes(B, Hq, Nq))
+
+
+def attn_bwd(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None, dv=None, workspace=None,
+             stream=None):
+    """Gradients (dq, dk, dv) of attn_fwd for the upstream gradient dout of o.
+    q, o, dout [B,Hq,Nq,d] and k, v [B,Hkv,Nk,d] bf16, lse fp32 [B,Hq,Nq]
+    (attn_fwd's outputs for the same q, k, v, scale, causal)."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("lse", lse, torch.float32)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q/o/dout [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] expected")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk_ = k.shape
+    if Bk != B or dk_ != d or tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("attn_bwd shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_dev(name, t, q.dtype)
+        if t.shape != ref.shape:
+            raise ValueError("%s must have %s's shape" % (name, "q" if ref is q else "k"))
+    need = attn_bwd_workspace_bytes(B, Hq, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_dev("workspace", workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nk, d, float(scale),
+                        int(bool(causal)), _dtype_code(q), workspace.data_ptr(), ws_bytes,
+                        _stream_handle(q, stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv
 
 
 def attn_decode_workspace_bytes(B, Hq, Hkv, max_seq_len, d, keys_per_split=0) -> int:

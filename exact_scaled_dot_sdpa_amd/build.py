@@ -28,12 +28,13 @@ def sources():
 KERNEL_SOURCES = {
     "prefill": ("prefill_bf16.hip", "kernels.h"),
     "decode": ("decode_bf16.hip", "kernels.h"),
+    "bwd": ("bwd_bf16.hip", "kernels.h"),
 }
 
 
 def source_digest(kernel=None) -> str:
     """Digest of the kernel sources: all of csrc/*.hip, *.h, or only those of
-    one logical kernel ("prefill", "decode").  Stored hardware-counter figures
+    one logical kernel ("prefill", "decode", "bwd").  Stored hardware-counter figures
     carry it, so that figures taken on other kernels are not reused."""
     if kernel is None:
         names = [n for n in sorted(os.listdir(CSRC)) if n.endswith((".hip", ".h"))]

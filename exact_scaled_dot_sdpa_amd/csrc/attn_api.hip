@@ -87,6 +87,42 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq)
+{
+    if (B < 0 || Hq < 1 || Nq < 0) return 0;
+    return (size_t)B * Hq * Nq * sizeof(float);
+}
+
+int attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse,
+             void *dq, void *dk, void *dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+             int dtype, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (B < 0 || Nq < 0 || Nk < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+    if (causal && Nq > Nk) return ATTN_ERR_INVALID_ARG;
+    if (!supported_d(d) || dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (B == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
+    if ((long long)B * Hq * Nq > 0x7fffffffLL || (long long)B * Hkv * Nk > 0x7fffffffLL)
+        return ATTN_ERR_UNSUPPORTED;
+    // every tensor the kernels touch must be present and 16-byte aligned
+    // (q and do are also read for dk / dv, k and v also for dq)
+    const bool rows_q = Nq > 0, rows_k = Nk > 0;
+    if (rows_q && (!q || !o || !dout || !dq || !lse)) return ATTN_ERR_INVALID_ARG;
+    if (rows_k && (!k || !v || !dk || !dv)) return ATTN_ERR_INVALID_ARG;
+    const void *p16[] = {q, k, v, o, dout, dq, dk, dv};
+    for (const void *p : p16)
+        if (p && !aligned(p, 16)) return ATTN_ERR_INVALID_ARG;
+    if (lse && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARG;
+    const size_t need = attn_bwd_workspace_bytes(B, Hq, Nq);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return ATTN_ERR_WORKSPACE;
+
+    attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float *)workspace, B, Hq, Hkv, Nq, Nk, d, scale,
+                    causal ? 1 : 0};
+    const hipError_t e = attn::launch_bwd_bf16(a, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_seq_len, int d, int keys_per_split)
 {
     if (!decode_sizes_ok(B, Hq, Hkv, max_seq_len) || !supported_d(d) || keys_per_split < 0) return 0;

@@ -34,9 +34,20 @@ struct DecodeArgs {
     int block_size, max_blocks, num_blocks;
 };
 
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;
+    void *dq, *dk, *dv;
+    float *ws_d;  // [B*Hq*Nq] fp32: do_i . o_i per row
+    int B, Hq, Hkv, Nq, Nk, d;
+    float scale;
+    int causal;
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_prefill_bf16(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_prefill_f32(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream);
 
 }  // namespace attn

@@ -5,8 +5,8 @@ from a seeded CPU ``torch.Generator`` (in fp32, then rounded to nearest even to
 the workload's element type) and describes the workload shapes.  The HIP path
 and the oracle consume the very same rounded values.
 
-Draw order is fixed: q, k, v for prefill; seq_lens, q, k_cache, v_cache for
-decode; seq_lens, q, k_pages, v_pages, block order for paged decode.
+Draw order is fixed: q, k, v for prefill (then do for the backward pass);
+seq_lens, q, k_cache, v_cache for decode; seq_lens, q, k_pages, v_pages, block order for paged decode.
 seq_lens are uniform integers in [lo, hi] inclusive.
 """
 from dataclasses import dataclass, field
@@ -108,6 +108,17 @@ def prefill_inputs(B, Hq, Hkv, Nq, Nk, d, dtype, seed):
     k = randn((B, Hkv, Nk, d), dtype, g)
     v = randn((B, Hkv, Nk, d), dtype, g)
     return q, k, v
+
+
+def bwd_inputs(B, Hq, Hkv, Nq, Nk, d, dtype, seed):
+    """q, k, v as ``prefill_inputs`` with the same seed, then the upstream
+    gradient do [B,Hq,Nq,d] (iid N(0, 1) like the rest)."""
+    g = _gen(seed)
+    q = randn((B, Hq, Nq, d), dtype, g)
+    k = randn((B, Hkv, Nk, d), dtype, g)
+    v = randn((B, Hkv, Nk, d), dtype, g)
+    do = randn((B, Hq, Nq, d), dtype, g)
+    return q, k, v, do
 
 
 def decode_inputs(B, Hq, Hkv, Lmax, d, dtype, seed, lo=512, hi=4096,

@@ -52,7 +52,7 @@ enum {
     ATTN_OK = 0,
     ATTN_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, non-finite scale */
     ATTN_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. d not 64/128) */
-    ATTN_ERR_WORKSPACE = 3,   /* decode workspace missing or too small */
+    ATTN_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or too small */
     ATTN_ERR_LAUNCH = 4       /* the HIP runtime reported an error at launch */
 };
 
@@ -84,6 +84,55 @@ enum {
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
              int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
              int causal, int dtype, hipStream_t stream);
+
+/*
+ * attn_bwd_workspace_bytes -- bytes of device workspace attn_bwd needs:
+ * one fp32 per query row (B * Hq * Nq * 4).  Returns 0 for invalid sizes.
+ */
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
+
+/*
+ * attn_bwd -- backward pass of attn_fwd: the gradients of
+ * O = softmax(scale * Q K^T [+ causal mask]) V with respect to q, k and v for
+ * an upstream gradient dout of o.
+ *
+ * The pages say that training needs these gradients ("Transformer 架构的数学与
+ * 计算深度解析", sec. 3.3) and that FlashAttention recomputes the weights
+ * instead of storing them ("Transformer 深度进阶：从矩阵视角到 FlashAttention
+ * 工程优化", the FlashAttention section); they print no formula.  The call
+ * returns the chain-rule derivative of the definition: with
+ * p_ij = exp(scale q_i.k_j - lse_i), D_i = dout_i . o_i, dp_ij = dout_i . v_j
+ * and ds_ij = p_ij (dp_ij - D_i):
+ *   dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,
+ *   dv_j = sum_i p_ij dout_i,
+ * sums over visible pairs only; for GQA, dk and dv of a K/V head sum over
+ * every query head of its group.
+ *
+ *   q, o, dout [B, Hq, Nq, d]   dtype (read): o and lse are attn_fwd's outputs
+ *   k, v       [B, Hkv, Nk, d]  dtype (read)     for the same q, k, v, scale,
+ *   lse        [B, Hq, Nq] fp32       (read)     causal
+ *   dq         [B, Hq, Nq, d]   dtype (written)
+ *   dk, dv     [B, Hkv, Nk, d]  dtype (written)
+ *   workspace  >= attn_bwd_workspace_bytes(B, Hq, Nq) bytes of caller-owned
+ *              device memory, 16-byte aligned; contents on entry do not
+ *              matter; calls that overlap in time must not share it.
+ *
+ * Sizes, head mapping, scale and causal alignment as attn_fwd.  Only
+ * dtype == ATTN_BF16 is implemented (ATTN_F32 returns ATTN_ERR_UNSUPPORTED);
+ * products take bf16 operands (the weights and ds rounded to nearest even)
+ * with fp32 accumulation, and the gradients are rounded to bf16.  Nq == 0
+ * gives dk = dv = 0; Nk == 0 gives dq = 0.  Tensors of an empty side may be
+ * NULL.  The result is deterministic (no atomics).
+ *
+ * Returns ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED,
+ * ATTN_ERR_WORKSPACE (nothing launched in these three cases) or
+ * ATTN_ERR_LAUNCH.
+ */
+int attn_bwd(const void *q, const void *k, const void *v, const void *o,
+             const void *dout, const float *lse, void *dq, void *dk, void *dv,
+             int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+             int causal, int dtype, void *workspace, size_t workspace_bytes,
+             hipStream_t stream);
 
 /*
  * attn_decode_workspace_bytes -- bytes of device workspace attn_decode needs

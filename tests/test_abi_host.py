@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert names == sorted(["attn_fwd", "attn_decode", "attn_decode_paged", "attn_decode_workspace_bytes",
-                            "attn_status_str"])
+                            "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str"])
     lib = ctypes.CDLL(E.lib_path())
     for n in names:
         assert hasattr(lib, n), "libattn.so does not export %s" % n
@@ -159,3 +159,46 @@ def test_decode_paged_workspace_is_the_contiguous_one():
     here)."""
     need = E.attn_decode_workspace_bytes(2, 8, 2, 8 * 32, 128)
     assert pdec(ws_bytes=need - 1) == E.ATTN_ERR_WORKSPACE
+
+
+def bwd(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, Hq=4, Hkv=2, Nq=64, Nk=64, d=128, scale=0.09,
+        causal=0, dtype=1, ws=P, ws_bytes=1 << 30):
+    return E.lib().attn_bwd(q, k, v, o, do, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, ws,
+                            ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=3, Hkv=2), E.ATTN_ERR_INVALID_ARG),
+    (dict(Hkv=0), E.ATTN_ERR_INVALID_ARG),
+    (dict(B=-1), E.ATTN_ERR_INVALID_ARG),
+    (dict(Nq=-1), E.ATTN_ERR_INVALID_ARG),
+    (dict(causal=1, Nq=65), E.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), E.ATTN_ERR_INVALID_ARG),
+    (dict(dtype=5), E.ATTN_ERR_INVALID_ARG),
+    (dict(dtype=0), E.ATTN_ERR_UNSUPPORTED),             # fp32 backward not implemented
+    (dict(d=32), E.ATTN_ERR_UNSUPPORTED),
+    (dict(lse=None), E.ATTN_ERR_INVALID_ARG),
+    (dict(do=None), E.ATTN_ERR_INVALID_ARG),
+    (dict(dq=None), E.ATTN_ERR_INVALID_ARG),
+    (dict(dv=None), E.ATTN_ERR_INVALID_ARG),
+    (dict(k=None), E.ATTN_ERR_INVALID_ARG),
+    (dict(o=P + 8), E.ATTN_ERR_INVALID_ARG),             # misaligned
+    (dict(dk=P + 2), E.ATTN_ERR_INVALID_ARG),
+    (dict(lse=P + 2), E.ATTN_ERR_INVALID_ARG),
+    (dict(ws=None), E.ATTN_ERR_WORKSPACE),
+    (dict(ws=P + 4), E.ATTN_ERR_WORKSPACE),
+    (dict(ws_bytes=1 * 4 * 64 * 4 - 1), E.ATTN_ERR_WORKSPACE),
+    (dict(Nq=1 << 16, Nk=1 << 16, Hq=1 << 15, Hkv=1 << 15), E.ATTN_ERR_UNSUPPORTED),  # rows >= 2^31
+    (dict(B=0), E.ATTN_OK),
+    (dict(Nq=0, Nk=0, q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk=None, dv=None, ws=None),
+     E.ATTN_OK),
+])
+def test_bwd_validation(kw, status):
+    assert bwd(**kw) == status
+
+
+def test_bwd_workspace_bytes():
+    assert E.attn_bwd_workspace_bytes(2, 8, 100) == 2 * 8 * 100 * 4
+    assert E.attn_bwd_workspace_bytes(0, 8, 100) == 0
+    assert E.attn_bwd_workspace_bytes(1, 0, 100) == 0
+    assert E.attn_bwd_workspace_bytes(1, 4, -1) == 0
