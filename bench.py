@@ -2,6 +2,7 @@
 """Benchmark of the attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-paged] [--no-rect]
+                    [--no-bwd]
 
 One step is one pass of the whole path over synthetic inputs already resident
 in device memory:
@@ -21,7 +22,10 @@ prefill rows on the host cores.  `decode_paged` times the decode workload
 against a paged cache (block table over a shuffled pool) on its own, after the
 timed steps; `chunked_prefill` (a 2048-token chunk over 8192 cached tokens,
 causal bottom-right) and `cross_attention` (2048 queries over 4096 keys,
-non-causal) time attn_fwd on the two rectangular workloads the same way.
+non-causal) time attn_fwd on the two rectangular workloads the same way;
+`backward` times attn_bwd (all three kernels) on the prefill workload with the
+forward's o and lse and a seeded upstream gradient, counting 2.5x the forward
+FLOPs (five matrix products per visible pair).
 """
 import argparse
 import json
@@ -48,10 +52,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target seconds of oracle work")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "bwd"], default=None,
                     help="run one kernel only (for profiling runs)")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache decode measurement")
     ap.add_argument("--paged-block-size", type=int, default=64)
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--no-rect", action="store_true",
                     help="skip the chunked-prefill and cross-attention measurements")
     return ap.parse_args()
@@ -136,6 +141,26 @@ def rect_prefill_line(E, A, I, dev, name, steps=20, warmup=50):
                       "causal": w.causal}, "note": w.note}
 
 
+def backward_line(E, A, I, dev, q, k, v, o, lse, w, steps=20, warmup=50):
+    """attn_bwd on the prefill workload, timed on its own."""
+    import torch
+
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed + 500)
+    do = I.randn(tuple(q.shape), w.dtype, g).to(dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(E.attn_bwd_workspace_bytes(w.B, w.Hq, w.Nq), dtype=torch.uint8, device=dev)
+    ms = timed_ms(lambda i: E.attn_bwd(q, k, v, o, do, lse, scale=w.scale, causal=w.causal, dq=dq, dk=dk, dv=dv,
+                                       workspace=ws), steps, warmup)
+    fl = A.bwd_flops(w.B, w.Hq, w.Nq, w.Nkv, w.d, w.causal)
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "avg_launch_ms": round(ms, 5), "flops_per_launch": fl,
+            "kernels": "bwd_pre_kernel<128> + bwd_dq_kernel<128,true> + bwd_dkdv_kernel<128,true>",
+            "note": "algorithmic FLOPs = 2.5x the forward's (S, dP, dV, dK, dQ products); the kernels "
+                    "recompute S and dP once more for dQ"}
+
+
 def cpu_baseline(q, k, v, w, target_s):
     """The oracle, as it stands, on a bounded sample of prefill rows."""
     import numpy as np
@@ -204,6 +229,7 @@ def main():
     wd = I.WORKLOADS["C5"]
     run_p = args.only in (None, "prefill")
     run_d = args.only in (None, "decode")
+    run_b = args.only in (None, "bwd") and not args.no_bwd
 
     # ---- inputs, resident in HBM before timing --------------------------
     q_cpu, k_cpu, v_cpu = I.workload_inputs("C4")
@@ -312,6 +338,11 @@ def main():
         }
     if run_d and not args.no_paged:
         out["decode_paged"] = paged_decode_line(E, A, I, dev, args.paged_block_size)
+    if run_b:
+        if not run_p:
+            prefill()
+            torch.cuda.synchronize()
+        out["backward"] = backward_line(E, A, I, dev, q, k, v, o, lse, wp)
     if run_p and not args.no_rect:
         out["chunked_prefill"] = rect_prefill_line(E, A, I, dev, "X1")
         out["cross_attention"] = rect_prefill_line(E, A, I, dev, "X2")

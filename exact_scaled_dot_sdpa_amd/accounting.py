@@ -32,6 +32,12 @@ def prefill_flops(B, Hq, Nq, Nk, d, causal) -> int:
     return 4 * d * B * Hq * visible_pairs(Nq, Nk, causal)
 
 
+def bwd_flops(B, Hq, Nq, Nk, d, causal) -> int:
+    """Backward-pass matrix FLOPs: five products per visible pair (the
+    recomputed scores, dP, dV, dK, dQ), 2*d each, i.e. 2.5x the forward."""
+    return 10 * d * B * Hq * visible_pairs(Nq, Nk, causal)
+
+
 def prefill_bytes(B, Hq, Hkv, Nq, Nk, d, dtype, with_lse=True) -> int:
     e = ELEM_BYTES[dtype]
     b = e * (B * Hq * Nq * d * 2 + 2 * B * Hkv * Nk * d)

@@ -90,7 +90,7 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq)
 {
     if (B < 0 || Hq < 1 || Nq < 0) return 0;
-    return (size_t)B * Hq * Nq * sizeof(float);
+    return (size_t)B * Hq * Nq * 2 * sizeof(float);
 }
 
 int attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse,

@@ -16,20 +16,26 @@
 //   dv_j  = sum_i p_ij do_i,  dk_j = scale sum_i ds_ij q_i,  dq_i = scale sum_j ds_ij k_j
 //
 // Three kernels, no atomics, deterministic:
-//   * bwd_pre_kernel: D_i for every row (HBM-bound, reads o and do once).
+//   * bwd_pre_kernel: D_i and lse_i * log2(e) for every row (HBM-bound,
+//     reads o and do once).
 //   * bwd_dq_kernel: a workgroup owns 128 query rows (32 per wave) of one
 //     query head; Q^T and dO^T stay in registers as MFMA B operands while
 //     K/V tiles of 64 keys stream through LDS (DMA, double-buffered).  Per
-//     tile: S^T = K Q^T and dP^T = V dO^T (v_mfma_f32_32x32x16_bf16), P^T and
-//     dS^T on the vector ALUs, then dQ^T += K^T dS^T, where dS^T (bf16) is
-//     used straight from the accumulator layout as the B operand and K^T is
-//     read from the row-major K tile with ds_read_b64_tr_b16.
-//   * bwd_dkdv_kernel: a workgroup owns 128 keys (32 per wave) of one K/V
-//     head; K^T and V^T stay in registers while Q / dO tiles of 64 rows of
-//     every query head of the GQA group stream through LDS, so dK and dV are
-//     summed over the group in registers.  Per tile: S = Q K^T, dP = dO V^T,
-//     P and dS, then dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read
-//     transposed from LDS.
+//     32-key half of a tile: S^T = K Q^T and dP^T = V dO^T
+//     (v_mfma_f32_32x32x16_bf16), P^T and dS^T on the vector ALUs, then
+//     dQ^T += K^T dS^T, where dS^T (bf16) is used straight from the
+//     accumulator layout as the B operand and K^T is read from the row-major
+//     K tile with ds_read_b64_tr_b16.  Two workgroups per CU (two waves per
+//     SIMD), so one wave's exp / VALU work hides behind another's MFMAs.
+//   * bwd_dkdv_kernel: a workgroup of 8 waves owns 128 keys of one K/V head;
+//     K^T (registers) and V^T (LDS) stay resident while Q / dO tiles of 64 rows of every
+//     query head of the GQA group stream through LDS, so dK and dV are summed
+//     over the group in registers (V's rows sit in LDS for the whole kernel
+//     to leave room for that).  Two waves share each 32-key slice, one
+//     per 32-row half of a tile (two waves per SIMD again), and add their
+//     partial sums through LDS at the end.  Per half tile: S = Q K^T,
+//     dP = dO V^T, P and dS, then dV^T += dO^T P and dK^T += Q^T dS with
+//     dO^T, Q^T read transposed from LDS.
 // Tiles that are read both row-wise (16 rows x one 16-byte chunk) and
 // transposed (4 rows x 4 chunks per 32 lanes) use one XOR swizzle of the
 // chunk index that keeps both patterns free of LDS bank conflicts.
@@ -59,6 +65,7 @@ constexpr int BM = 128;   // dq kernel: query rows per workgroup
 constexpr int BN = 64;    // dq kernel: keys per tile
 constexpr int BKN = 128;  // dkdv kernel: keys per workgroup
 constexpr int BQ = 64;    // dkdv kernel: query rows per tile
+constexpr int KNW = 8;    // dkdv kernel: waves per workgroup
 constexpr float LOG2E = 1.44269504088896340736f;
 
 template <int D>
@@ -92,21 +99,21 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 // ROWS rows of D bf16 from base[row0 ..] into an LDS tile, row-major with
 // the chunk swizzle folded into voff (the lane's byte offset; see the
 // kernels).  One wave-wide buffer_load_dwordx4 ... lds fills RPW rows; wave w
-// fills rows (4r + w) * RPW .. in round r.  The descriptor ends at the last
+// of NW fills rows (NW r + w) * RPW .. in round r.  The descriptor ends at the last
 // row of the tensor, so rows past it land as zeros.
-template <int D, int ROWS>
+template <int D, int ROWS, int NW>
 __device__ __forceinline__ void dma_tile(const __bf16 *base, int row0, int nrows, __bf16 *dst, int voff,
                                          int wave_s) {
     using C = Cfg<D>;
-    constexpr int ROUNDS = ROWS / (4 * C::RPW);
-    constexpr int ROUND_BYTES = 4 * C::RPW * D * 2;
-    static_assert(ROUNDS * 4 * C::RPW == ROWS, "tile split");
+    constexpr int ROUNDS = ROWS / (NW * C::RPW);
+    constexpr int ROUND_BYTES = NW * C::RPW * D * 2;
+    static_assert(ROUNDS * NW * C::RPW == ROWS, "tile split");
     const int left = nrows - row0;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(base + (size_t)row0 * D), (short)0, (left < ROWS ? left : ROWS) * D * 2, 0x00020000);
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
-        __bf16 *d = dst + (r * 4 + wave_s) * C::RPW * D;
+        __bf16 *d = dst + (r * NW + wave_s) * C::RPW * D;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)d, 16, voff, r * ROUND_BYTES, 0, 0);
     }
 }
@@ -183,10 +190,11 @@ __device__ __forceinline__ int xcd_remap(int L, int total) {
 }
 
 // ---------------------------------------------------------------------------
-// D_i = do_i . o_i for every row (fp32).
+// D_i = do_i . o_i and lse_i * log2(e) for every row (fp32).
 template <int D>
 __global__ __launch_bounds__(NTHR) void bwd_pre_kernel(const __bf16 *__restrict__ O,
-                                                       const __bf16 *__restrict__ dO, float *__restrict__ Dv,
+                                                       const __bf16 *__restrict__ dO, const float *__restrict__ LSE,
+                                                       float *__restrict__ Dv, float *__restrict__ L2,
                                                        long long rows) {
     constexpr int LPR = D / 8;  // lanes per row
     const long long t = (long long)blockIdx.x * NTHR + threadIdx.x;
@@ -201,14 +209,17 @@ __global__ __launch_bounds__(NTHR) void bwd_pre_kernel(const __bf16 *__restrict_
     }
 #pragma unroll
     for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
-    if (row < rows && part == 0) Dv[row] = acc;
+    if (row < rows && part == 0) {
+        Dv[row] = acc;
+        L2[row] = LSE[row] * LOG2E;
+    }
 }
 
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(NTHR, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(NTHR, 2) void bwd_dq_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
-    const __bf16 *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Dv,
+    const __bf16 *__restrict__ dO, const float *__restrict__ L2, const float *__restrict__ Dv,
     __bf16 *__restrict__ dQ, int Hq, int Hkv, int Nq, int Nk, float sl2, float scale, int n_qtiles, int total)
 {
     using C = Cfg<D>;
@@ -250,7 +261,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_dq_kernel(
             qf[s] = sq[2 * s];
             df[s] = sd[2 * s];
         }
-        lse2 = LSE[qrow0 + qi] * LOG2E;
+        lse2 = L2[qrow0 + qi];
         dd = Dv[qrow0 + qi];
     } else {
 #pragma unroll
@@ -290,8 +301,8 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_dq_kernel(
     auto kbuf = [&](int j) { return (j & 1) ? sK1 : sK0; };
     auto vbuf = [&](int j) { return (j & 1) ? sV1 : sV0; };
     auto load = [&](int j) {
-        dma_tile<D, BN>(Kh, j * BN, Nk, kbuf(j), voff_k, wave_s);
-        dma_tile<D, BN>(Vh, j * BN, Nk, vbuf(j), voff_v, wave_s);
+        dma_tile<D, BN, 4>(Kh, j * BN, Nk, kbuf(j), voff_k, wave_s);
+        dma_tile<D, BN, 4>(Vh, j * BN, Nk, vbuf(j), voff_v, wave_s);
     };
 
     if (ntiles > 0) load(0);
@@ -303,43 +314,33 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_dq_kernel(
         if (CAUSAL && j0 > wave_first_row + 31 + off) continue;  // no row of this wave sees tile j
         const __bf16 *sk = kbuf(j), *sv = vbuf(j);
 
-        // S^T = K Q^T and dP^T = V dO^T, keys in two halves of 32
-        f32x16 st[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-        for (int s = 0; s < C::KS; ++s) {
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(sk + kt * 32 * D + k_off[s]);
-                st[kt] = mfma(ka, qf[s], st[kt]);
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < C::KS; ++s) {
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const bf16x8 va = *reinterpret_cast<const bf16x8 *>(sv + kt * 32 * D + v_off[s]);
-                dp[kt] = mfma(va, df[s], dp[kt]);
-            }
-        }
-        // P^T and dS^T = P^T (dP^T - D) for this lane's row; lane (n, g)
-        // holds keys j0 + 32 kt + 8 (r / 4) + 4 g + r % 4
+        // one 32-key half at a time: S^T = K Q^T, dP^T = V dO^T, then P^T and
+        // dS^T = P^T (dP^T - D) for this lane's row (lane (n, g) holds keys
+        // j0 + 32 kt + 8 (r / 4) + 4 g + r % 4), then dQ^T += K^T dS^T
         const bool need_mask = (j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > wave_first_row + off);
         const int rel = lim - j0 - 4 * g;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
+            f32x16 st = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int s = 0; s < C::KS; ++s) {
+                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(sk + kt * 32 * D + k_off[s]);
+                st = mfma(ka, qf[s], st);
+            }
+#pragma unroll
+            for (int s = 0; s < C::KS; ++s) {
+                const bf16x8 va = *reinterpret_cast<const bf16x8 *>(sv + kt * 32 * D + v_off[s]);
+                dp = mfma(va, df[s], dp);
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float p = __builtin_amdgcn_exp2f(fmaf(st[kt][r], sl2, -lse2));
+                float p = __builtin_amdgcn_exp2f(fmaf(st[r], sl2, -lse2));
                 if (need_mask && kt * 32 + 8 * (r >> 2) + (r & 3) > rel) p = 0.f;
-                st[kt][r] = p * (dp[kt][r] - dd);
+                st[r] = p * (dp[r] - dd);
             }
-        }
-        // dQ^T += K^T dS^T
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                const bf16x8 bs = pack_b(st[kt], hh);
+                const bf16x8 bs = pack_b(st, hh);
 #pragma unroll
                 for (int cb = 0; cb < C::CB; ++cb) acc[cb] = mfma(tr_frag<D>(sk, kt_off, cb, 2 * kt + hh), bs, acc[cb]);
             }
@@ -363,10 +364,14 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// 8 waves: wave w owns keys k0 + 32 (w % 4) .. + 31 and the query rows
+// 32 (w / 4) .. + 31 of every tile, so two waves (one per SIMD pair slot)
+// accumulate partial dK / dV of the same keys; the partials are summed
+// through LDS at the end.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(NTHR, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(KNW * 64) void bwd_dkdv_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
-    const __bf16 *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Dv,
+    const __bf16 *__restrict__ dO, const float *__restrict__ L2, const float *__restrict__ Dv,
     __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, int Hq, int Hkv, int Nq, int Nk, float sl2, float scale,
     int n_ktiles, int total)
 {
@@ -379,6 +384,7 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_dkdv_kernel(
     __shared__ __attribute__((aligned(256))) float sL1[BQ];
     __shared__ __attribute__((aligned(256))) float sE0[BQ];
     __shared__ __attribute__((aligned(256))) float sE1[BQ];
+    __shared__ __attribute__((aligned(1024))) __bf16 sV[BKN * D];  // the workgroup's V rows
 
     // work item: (batch, KV head) outermost, then key tile (heaviest causal
     // tile, the first, first)
@@ -392,26 +398,22 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_dkdv_kernel(
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 31, g = lane >> 5;
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int kw = wave & 3, qh = wave >> 2;  // key slice, query half
     const int off = Nk - Nq;
-    const int wk0 = k0 + wave * 32;  // this wave's first key
-    const int kj = wk0 + n;          // this lane's key
+    const int wk0 = k0 + kw * 32;  // this wave's first key
+    const int kj = wk0 + n;        // this lane's key
 
+    // K^T operands in registers; V rows in LDS (registers are the limit at
+    // two waves per SIMD), both for the whole kernel
     const size_t krow0 = (size_t)(b * Hkv + hk) * Nk;
-    bf16x8 kf[C::KS], vf[C::KS];
+    bf16x8 kf[C::KS];
     if (kj < Nk) {
         const bf16x8 *sk = reinterpret_cast<const bf16x8 *>(K + (krow0 + kj) * D + 8 * g);
-        const bf16x8 *sv = reinterpret_cast<const bf16x8 *>(V + (krow0 + kj) * D + 8 * g);
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s) {
-            kf[s] = sk[2 * s];
-            vf[s] = sv[2 * s];
-        }
+        for (int s = 0; s < C::KS; ++s) kf[s] = sk[2 * s];
     } else {
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s) {
-            kf[s] = bf16x8{};
-            vf[s] = bf16x8{};
-        }
+        for (int s = 0; s < C::KS; ++s) kf[s] = bf16x8{};
     }
 
     // query tiles that see some key of the workgroup: rows >= k0 - off
@@ -427,9 +429,11 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_dkdv_kernel(
 
     const int ld_row = wave * C::RPW + lane / C::CH, ld_slot = lane % C::CH;
     const int voff = (ld_row * D + ((ld_slot ^ swz_rt<D>(ld_row)) * 8)) * 2;
-    int r_off[C::KS];
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s) r_off[s] = n * D + (((2 * s + g) ^ swz_rt<D>(n)) * 8);
+    const int voff_v = (ld_row * D + ((ld_slot ^ swz_rows<D>(ld_row)) * 8)) * 2;
+    // row reads of this wave's 32 query rows (row 32 qh + n) and of its keys'
+    // V rows (row 32 kw + n), chunk 2s + g
+    const int rq_base = (qh * 32 + n) * D, rv_base = (kw * 32 + n) * D;
+    const int x_rt = g ^ swz_rt<D>(n), x_rows = g ^ swz_rows<D>(n);
     const TrLane trl(lane);
     const TrOffsets<D> t_off(trl);
 
@@ -447,81 +451,102 @@ __global__ __launch_bounds__(NTHR, 1) void bwd_dkdv_kernel(
     auto load = [&](int u) {
         const int gq = u / nt, qt = t_start + u % nt;
         const size_t qrow0 = (size_t)(b * Hq + hk * G + gq) * Nq;
-        dma_tile<D, BQ>(Q + qrow0 * D, qt * BQ, Nq, qbuf(u), voff, wave_s);
-        dma_tile<D, BQ>(dO + qrow0 * D, qt * BQ, Nq, dbuf(u), voff, wave_s);
+        dma_tile<D, BQ, KNW>(Q + qrow0 * D, qt * BQ, Nq, qbuf(u), voff, wave_s);
+        dma_tile<D, BQ, KNW>(dO + qrow0 * D, qt * BQ, Nq, dbuf(u), voff, wave_s);
         if (wave_s == 0) {
-            dma_row_vals(LSE + qrow0, qt * BQ, Nq, lbuf(u), lane);
+            dma_row_vals(L2 + qrow0, qt * BQ, Nq, lbuf(u), lane);
             dma_row_vals(Dv + qrow0, qt * BQ, Nq, ebuf(u), lane);
         }
     };
 
-    if (steps > 0) load(0);
+    if (steps > 0) {
+        dma_tile<D, BKN, KNW>(V + krow0 * D, k0, Nk, sV, voff_v, wave_s);
+        load(0);
+    }
     for (int u = 0; u < steps; ++u) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (u + 1 < steps) load(u + 1);
-        const int q0 = (t_start + u % nt) * BQ;
-        if (CAUSAL && q0 + BQ - 1 + off < wk0) continue;  // no row of the tile sees this wave's keys
+        const int qb = (t_start + u % nt) * BQ + qh * 32;  // this wave's first query row
+        if (qb >= Nq || (CAUSAL && qb + 31 + off < wk0)) continue;  // none of its rows sees these keys
         const __bf16 *sq = qbuf(u), *sd = dbuf(u);
-        const float *sl = lbuf(u), *se = ebuf(u);
+        const float *sl = lbuf(u) + qh * 32, *se = ebuf(u) + qh * 32;
 
-        // S = Q K^T and dP = dO V^T, query rows in two halves of 32
-        f32x16 sc[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+        // S = Q K^T and dP = dO V^T for 32 rows x 32 keys
+        f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s) {
+        for (int s = 0; s < C::KS; ++s)
+            sc = mfma(*reinterpret_cast<const bf16x8 *>(sq + rq_base + (((2 * s) ^ x_rt) * 8)), kf[s], sc);
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(sq + qt * 32 * D + r_off[s]);
-                sc[qt] = mfma(qa, kf[s], sc[qt]);
-            }
-        }
+        for (int s = 0; s < C::KS; ++s)
+            dp = mfma(*reinterpret_cast<const bf16x8 *>(sd + rq_base + (((2 * s) ^ x_rt) * 8)),
+                      *reinterpret_cast<const bf16x8 *>(sV + rv_base + (((2 * s) ^ x_rows) * 8)), dp);
+        // P and dS: lane (n, g) holds key kj and rows qb + 8 rr + 4 g + i
+        const bool need_mask = (qb + 32 > Nq) || (wk0 + 32 > Nk) || (CAUSAL && wk0 + 31 > qb + off);
+        u32x4 bp[2];
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s) {
+        for (int rr = 0; rr < 4; ++rr) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sl + 8 * rr + 4 * g);
+            const f32x4 e4 = *reinterpret_cast<const f32x4 *>(se + 8 * rr + 4 * g);
+            float p[4];
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt) {
-                const bf16x8 da = *reinterpret_cast<const bf16x8 *>(sd + qt * 32 * D + r_off[s]);
-                dp[qt] = mfma(da, vf[s], dp[qt]);
-            }
-        }
-        // P and dS: lane (n, g) holds key kj and rows q0 + 32 qt + 8 rr + 4 g + i
-        const bool need_mask = (q0 + BQ > Nq) || (wk0 + 32 > Nk) || (CAUSAL && wk0 + 31 > q0 + off);
-        f32x16 pp[2];
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sl + 32 * qt + 8 * rr + 4 * g);
-                const f32x4 e4 = *reinterpret_cast<const f32x4 *>(se + 32 * qt + 8 * rr + 4 * g);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * rr + i;
-                    float p = __builtin_amdgcn_exp2f(fmaf(sc[qt][r], sl2, -l4[i] * LOG2E));
-                    if (need_mask) {
-                        const int qrow = q0 + 32 * qt + 8 * rr + 4 * g + i;
-                        if (qrow >= Nq || kj >= Nk || (CAUSAL && kj > qrow + off)) p = 0.f;
-                    }
-                    pp[qt][r] = p;
-                    sc[qt][r] = p * (dp[qt][r] - e4[i]);
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * rr + i;
+                p[i] = __builtin_amdgcn_exp2f(fmaf(sc[r], sl2, -l4[i]));
+                if (need_mask) {
+                    const int qrow = qb + 8 * rr + 4 * g + i;
+                    if (qrow >= Nq || kj >= Nk || (CAUSAL && kj > qrow + off)) p[i] = 0.f;
                 }
+                sc[r] = p[i] * (dp[r] - e4[i]);
             }
+            bp[rr >> 1][2 * (rr & 1)] = pack_bf16(p[0], p[1]);
+            bp[rr >> 1][2 * (rr & 1) + 1] = pack_bf16(p[2], p[3]);
         }
-        // dV^T += dO^T P and dK^T += Q^T dS
+        // dV^T += dO^T P and dK^T += Q^T dS over this wave's 32 rows
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
+        for (int hh = 0; hh < 2; ++hh) {
+            const bf16x8 bpv = __builtin_bit_cast(bf16x8, bp[hh]);
+            const bf16x8 bs = pack_b(sc, hh);
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const bf16x8 bp = pack_b(pp[qt], hh);
-                const bf16x8 bs = pack_b(sc[qt], hh);
-#pragma unroll
-                for (int cb = 0; cb < C::CB; ++cb) {
-                    accv[cb] = mfma(tr_frag<D>(sd, t_off, cb, 2 * qt + hh), bp, accv[cb]);
-                    acck[cb] = mfma(tr_frag<D>(sq, t_off, cb, 2 * qt + hh), bs, acck[cb]);
-                }
+            for (int cb = 0; cb < C::CB; ++cb) {
+                accv[cb] = mfma(tr_frag<D>(sd, t_off, cb, 2 * qh + hh), bpv, accv[cb]);
+                acck[cb] = mfma(tr_frag<D>(sq, t_off, cb, 2 * qh + hh), bs, acck[cb]);
             }
         }
     }
 
-    if (kj < Nk) {
+    // sum the two query halves' partials through LDS (the tile buffers are
+    // free once every wave has passed the barrier): wave kw + 4 stores, wave
+    // kw adds; element i of lane l at red[i * 64 + l]
+    float *red = reinterpret_cast<float *>(kw == 0 ? sQ0 : kw == 1 ? sQ1 : kw == 2 ? sD0 : sD1);
+    static_assert(C::CB * 16 * 64 * 4 <= BQ * D * 2, "reduction fits a tile buffer");
+    __syncthreads();
+    if (qh == 1) {
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[(cb * 16 + r) * 64 + lane] = acck[cb][r];
+    }
+    __syncthreads();
+    if (qh == 0) {
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acck[cb][r] += red[(cb * 16 + r) * 64 + lane];
+    }
+    __syncthreads();
+    if (qh == 1) {
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[(cb * 16 + r) * 64 + lane] = accv[cb][r];
+    }
+    __syncthreads();
+    if (qh == 0 && kj < Nk) {
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) accv[cb][r] += red[(cb * 16 + r) * 64 + lane];
         __bf16 *rk = dK + (krow0 + kj) * D;
         __bf16 *rv = dV + (krow0 + kj) * D;
 #pragma unroll
@@ -549,22 +574,24 @@ hipError_t launch(const BwdArgs &a, hipStream_t stream) {
         const long long blocks = (threads + NTHR - 1) / NTHR;
         if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)blocks), dim3(NTHR), 0, stream,
-                           (const __bf16 *)a.o, (const __bf16 *)a.dout, a.ws_d, rows);
+                           (const __bf16 *)a.o, (const __bf16 *)a.dout, a.lse, a.ws_d, a.ws_d + rows, rows);
         const int n_qtiles = (a.Nq + BM - 1) / BM;
         const long long total = (long long)a.B * a.Hq * n_qtiles;
         if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)total), dim3(NTHR), 0, stream,
                            (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
-                           (const __bf16 *)a.dout, a.lse, (const float *)a.ws_d, (__bf16 *)a.dq, a.Hq, a.Hkv,
+                           (const __bf16 *)a.dout, (const float *)(a.ws_d + rows), (const float *)a.ws_d,
+                           (__bf16 *)a.dq, a.Hq, a.Hkv,
                            a.Nq, a.Nk, sl2, a.scale, n_qtiles, (int)total);
     }
     const int n_ktiles = (a.Nk + BKN - 1) / BKN;
     const long long total_k = (long long)a.B * a.Hkv * n_ktiles;
     if (total_k > 0) {
         if (total_k > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)total_k), dim3(NTHR), 0, stream,
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)total_k), dim3(KNW * 64), 0, stream,
                            (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
-                           (const __bf16 *)a.dout, a.lse, (const float *)a.ws_d, (__bf16 *)a.dk, (__bf16 *)a.dv,
+                           (const __bf16 *)a.dout, (const float *)(a.ws_d + rows), (const float *)a.ws_d,
+                           (__bf16 *)a.dk, (__bf16 *)a.dv,
                            a.Hq, a.Hkv, a.Nq, a.Nk, sl2, a.scale, n_ktiles, (int)total_k);
     }
     return hipGetLastError();

@@ -38,7 +38,7 @@ struct BwdArgs {
     const void *q, *k, *v, *o, *dout;
     const float *lse;
     void *dq, *dk, *dv;
-    float *ws_d;  // [B*Hq*Nq] fp32: do_i . o_i per row
+    float *ws_d;  // [2, B*Hq*Nq] fp32: do_i . o_i, then lse_i * log2(e), per row
     int B, Hq, Hkv, Nq, Nk, d;
     float scale;
     int causal;

@@ -87,7 +87,7 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 
 /*
  * attn_bwd_workspace_bytes -- bytes of device workspace attn_bwd needs:
- * one fp32 per query row (B * Hq * Nq * 4).  Returns 0 for invalid sizes.
+ * two fp32 per query row (B * Hq * Nq * 8).  Returns 0 for invalid sizes.
  */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
 

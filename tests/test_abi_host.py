@@ -187,7 +187,7 @@ def bwd(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, Hq=4, Hkv=2, Nq=
     (dict(lse=P + 2), E.ATTN_ERR_INVALID_ARG),
     (dict(ws=None), E.ATTN_ERR_WORKSPACE),
     (dict(ws=P + 4), E.ATTN_ERR_WORKSPACE),
-    (dict(ws_bytes=1 * 4 * 64 * 4 - 1), E.ATTN_ERR_WORKSPACE),
+    (dict(ws_bytes=1 * 4 * 64 * 8 - 1), E.ATTN_ERR_WORKSPACE),
     (dict(Nq=1 << 16, Nk=1 << 16, Hq=1 << 15, Hkv=1 << 15), E.ATTN_ERR_UNSUPPORTED),  # rows >= 2^31
     (dict(B=0), E.ATTN_OK),
     (dict(Nq=0, Nk=0, q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk=None, dv=None, ws=None),
@@ -198,7 +198,7 @@ def test_bwd_validation(kw, status):
 
 
 def test_bwd_workspace_bytes():
-    assert E.attn_bwd_workspace_bytes(2, 8, 100) == 2 * 8 * 100 * 4
+    assert E.attn_bwd_workspace_bytes(2, 8, 100) == 2 * 8 * 100 * 8
     assert E.attn_bwd_workspace_bytes(0, 8, 100) == 0
     assert E.attn_bwd_workspace_bytes(1, 0, 100) == 0
     assert E.attn_bwd_workspace_bytes(1, 4, -1) == 0

@@ -45,3 +45,8 @@ def test_workload_figures():
     sl = [512, 4096]
     assert A.decode_bytes(sl, 32, 8, 128, "bf16") == 4096 * sum(sl) + 2 * 2 * 32 * 128 * 2 + 4 * 2 + 4 * 2 * 32
     assert A.decode_flops(sl, 32, 128) == 4 * 128 * 32 * sum(sl)
+
+
+def test_bwd_flops_is_two_and_a_half_forward():
+    for (Nq, Nk, causal) in ((100, 100, True), (64, 333, True), (50, 70, False)):
+        assert 2 * A.bwd_flops(2, 4, Nq, Nk, 64, causal) == 5 * A.prefill_flops(2, 4, Nq, Nk, 64, causal)
