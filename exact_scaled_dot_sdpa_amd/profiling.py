@@ -14,6 +14,7 @@ exactly that many bytes.  The JSON records each kernel's source digest;
 bench.py reports a kernel's bytes only while its sources are unchanged.
 """
 import argparse
+import re
 import csv
 import json
 import os
@@ -24,14 +25,22 @@ KERNELS = {
     # logical kernel -> substrings of the dispatched kernel names that make one launch
     "prefill": ["prefill_bf16_kernel"],
     "decode": ["decode_chunk_kernel", "decode_merge_kernel"],
+    "bwd": ["bwd_pre_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel"],
 }
 COPY_KERNEL = "copyBuffer"
 
 
 def _short(name):
-    for key in ("prefill_bf16_kernel", "prefill_f32_kernel", "decode_chunk_kernel", "decode_merge_kernel"):
-        if key in name:
-            return key
+    """The kernel's own identifier: the length-prefixed name after the
+    namespaces of an Itanium-mangled symbol, or the function name of a
+    demangled one."""
+    m = re.match(r"_ZN(?:\d+attn)?(?:12_GLOBAL__N_1)?(\d+)", name)
+    if m:
+        n = int(m.group(1))
+        return name[m.end():m.end() + n]
+    m = re.search(r"(\w+)<", name)
+    if m:
+        return m.group(1)
     return name[:60]
 
 
