@@ -2,7 +2,7 @@
 """Benchmark of the attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-paged] [--no-rect]
-                    [--no-bwd]
+                    [--no-bwd] [--no-fp8]
 
 One step is one pass of the whole path over synthetic inputs already resident
 in device memory:
@@ -25,7 +25,10 @@ causal bottom-right) and `cross_attention` (2048 queries over 4096 keys,
 non-causal) time attn_fwd on the two rectangular workloads the same way;
 `backward` times attn_bwd (all three kernels) on the prefill workload with the
 forward's o and lse and a seeded upstream gradient, counting 2.5x the forward
-FLOPs (five matrix products per visible pair).
+FLOPs (five matrix products per visible pair); `fp8_prefill` times
+attn_fwd_fp8 on the prefill workload's shape with e4m3 inputs (scores on the
+fp8 MFMA, P V on the bf16 MFMA; its peak is the 3.33 PFLOP/s that half the
+FLOPs at 5.0 and half at 2.5 PFLOP/s allow).
 """
 import argparse
 import json
@@ -38,6 +41,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (published)
 METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak (prefill); KV-cache GB/s & % HBM (decode)"
 N_REPLICAS = 4
 
@@ -52,11 +56,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target seconds of oracle work")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
-    ap.add_argument("--only", choices=["prefill", "decode", "bwd"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "bwd", "fp8"], default=None,
                     help="run one kernel only (for profiling runs)")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache decode measurement")
     ap.add_argument("--paged-block-size", type=int, default=64)
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass measurement")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 prefill measurement")
     ap.add_argument("--no-rect", action="store_true",
                     help="skip the chunked-prefill and cross-attention measurements")
     return ap.parse_args()
@@ -161,6 +166,26 @@ def backward_line(E, A, I, dev, q, k, v, o, lse, w, steps=20, warmup=50):
                     "recompute S and dP once more for dQ"}
 
 
+def fp8_prefill_line(E, A, I, dev, steps=20, warmup=50):
+    """attn_fwd_fp8 on the prefill workload's shape (e4m3 q, k, v), timed on its own."""
+    import torch
+
+    w = I.WORKLOADS["C4"]
+    q, k, v = (t.to(dev) for t in I.prefill_inputs(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.d, "fp8", w.seed))
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    ms = timed_ms(lambda i: E.attn_fwd_fp8(q, k, v, scale=w.scale, causal=w.causal, o=o, lse=lse), steps, warmup)
+    fl = A.prefill_flops(w.B, w.Hq, w.Nq, w.Nkv, w.d, w.causal)
+    tf = fl / (ms * 1e-3) / 1e12
+    peak = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "frac": round(tf / peak, 4), "peak": round(peak, 1),
+            "avg_launch_ms": round(ms, 5), "flops_per_launch": fl,
+            "bytes_per_launch": A.prefill_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.d, "fp8"),
+            "kernel": "prefill_fp8_kernel<128,true>",
+            "note": "e4m3 q, k, v (seeded N(0,1) rounded to e4m3); scores on the fp8 MFMA, P V on the bf16 MFMA "
+                    "with V widened exactly; bf16 output"}
+
+
 def cpu_baseline(q, k, v, w, target_s):
     """The oracle, as it stands, on a bounded sample of prefill rows."""
     import numpy as np
@@ -230,6 +255,7 @@ def main():
     run_p = args.only in (None, "prefill")
     run_d = args.only in (None, "decode")
     run_b = args.only in (None, "bwd") and not args.no_bwd
+    run_8 = args.only in (None, "fp8") and not args.no_fp8
 
     # ---- inputs, resident in HBM before timing --------------------------
     q_cpu, k_cpu, v_cpu = I.workload_inputs("C4")
@@ -343,6 +369,8 @@ def main():
             prefill()
             torch.cuda.synchronize()
         out["backward"] = backward_line(E, A, I, dev, q, k, v, o, lse, wp)
+    if run_8:
+        out["fp8_prefill"] = fp8_prefill_line(E, A, I, dev)
     if run_p and not args.no_rect:
         out["chunked_prefill"] = rect_prefill_line(E, A, I, dev, "X1")
         out["cross_attention"] = rect_prefill_line(E, A, I, dev, "X2")

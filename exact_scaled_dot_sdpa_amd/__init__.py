@@ -8,6 +8,7 @@ provides device memory and streams.
 Functions carry the names of the C entry points:
 
     attn_fwd(q, k, v, scale=None, causal=False, o=None, lse=None, return_lse=True)
+    attn_fwd_fp8(q, k, v, scale=None, v_scale=1.0, causal=False, o=None, lse=None, return_lse=True)
     attn_decode(q, k_cache, v_cache, seq_lens, scale=None, o=None, lse=None,
                 workspace=None, keys_per_split=0, return_lse=True)
     attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, o=None,
@@ -36,6 +37,7 @@ from ._binding import (  # noqa: F401
     attn_decode_paged,
     attn_decode_workspace_bytes,
     attn_fwd,
+    attn_fwd_fp8,
     attn_status_str,
     lib,
     lib_path,
@@ -43,6 +45,7 @@ from ._binding import (  # noqa: F401
 
 __all__ = [
     "attn_fwd",
+    "attn_fwd_fp8",
     "attn_decode",
     "attn_decode_paged",
     "attn_decode_workspace_bytes",

@@ -41,6 +41,8 @@ def lib():
     L.attn_decode.restype = i
     L.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp, sz, vp]
     L.attn_decode_paged.restype = i
+    L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, i, vp]
+    L.attn_fwd_fp8.restype = i
     L.attn_bwd_workspace_bytes.argtypes = [i, i, i]
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_bwd.argtypes = [vp] * 9 + [i] * 6 + [f, i, i, vp, sz, vp]
@@ -118,6 +120,40 @@ def attn_fwd(q, k, v, scale=None, causal=False, o=None, lse=None, return_lse=Tru
                         _stream_handle(q, stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd")
+    return (o, lse) if return_lse else o
+
+
+def attn_fwd_fp8(q, k, v, scale=None, v_scale=1.0, causal=False, o=None, lse=None, return_lse=True, stream=None):
+    """attn_fwd for q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] in torch.float8_e4m3fn:
+    O = v_scale * softmax(scale * Q K^T [+ causal mask]) V in bf16.  Returns
+    (o, lse) or o."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, torch.float8_e4m3fn)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] expected")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if Bk != B or dk != d:
+        raise ValueError("batch or head-dim mismatch: q %s k %s" % (tuple(q.shape), tuple(k.shape)))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    _check_dev("o", o, torch.bfloat16)
+    if tuple(o.shape) != tuple(q.shape):
+        raise ValueError("o must have q's shape")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_dev("lse", lse, torch.float32)
+        if tuple(lse.shape) != (B, Hq, Nq):
+            raise ValueError("lse must be [B,Hq,Nq]")
+    st = lib().attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                            lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Nq, Nk, d, float(scale),
+                            float(v_scale), int(bool(causal)), _stream_handle(q, stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_fp8")
     return (o, lse) if return_lse else o
 
 

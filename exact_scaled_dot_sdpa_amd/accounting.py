@@ -16,7 +16,7 @@ Byte formulas from the pages (cited by title and section):
     sec. 3.2 (LLaMA-7B: 32 MB per layer at n=2048 in FP16) and sec. 7.3
     (32 layers at n=8192: about 4 GB).
 """
-ELEM_BYTES = {"f32": 4, "bf16": 2}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
 
 
 def visible_pairs(Nq: int, Nk: int, causal: bool) -> int:
@@ -39,8 +39,10 @@ def bwd_flops(B, Hq, Nq, Nk, d, causal) -> int:
 
 
 def prefill_bytes(B, Hq, Hkv, Nq, Nk, d, dtype, with_lse=True) -> int:
+    """Read q, k, v once and write o (and lse); fp8 inputs give a bf16 o."""
     e = ELEM_BYTES[dtype]
-    b = e * (B * Hq * Nq * d * 2 + 2 * B * Hkv * Nk * d)
+    eo = 2 if dtype == "fp8" else e
+    b = e * (B * Hq * Nq * d + 2 * B * Hkv * Nk * d) + eo * B * Hq * Nq * d
     if with_lse:
         b += 4 * B * Hq * Nq
     return b

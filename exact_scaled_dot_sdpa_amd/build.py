@@ -29,6 +29,7 @@ KERNEL_SOURCES = {
     "prefill": ("prefill_bf16.hip", "kernels.h"),
     "decode": ("decode_bf16.hip", "kernels.h"),
     "bwd": ("bwd_bf16.hip", "kernels.h"),
+    "fp8": ("prefill_fp8.hip", "kernels.h"),
 }
 
 

@@ -87,6 +87,25 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+int attn_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int Nq,
+                 int Nk, int d, float scale, float v_scale, int causal, hipStream_t stream)
+{
+    if (B < 0 || Nq < 0 || Nk < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+    if (!isfinite(scale) || !isfinite(v_scale)) return ATTN_ERR_INVALID_ARG;
+    if (causal && Nq > Nk) return ATTN_ERR_INVALID_ARG;
+    if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;
+    if (B == 0 || Nq == 0) return ATTN_OK;
+    if (!q || !o) return ATTN_ERR_INVALID_ARG;
+    if (Nk > 0 && (!k || !v)) return ATTN_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(o, 16) || (k && !aligned(k, 16)) || (v && !aligned(v, 16)))
+        return ATTN_ERR_INVALID_ARG;
+    if (lse && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARG;
+    if ((long long)B * Hq * Nq > 0x7fffffffLL || (long long)B * Hkv * Nk > 0x7fffffffLL)
+        return ATTN_ERR_UNSUPPORTED;
+    attn::Fp8FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, v_scale, causal ? 1 : 0};
+    return attn::launch_prefill_fp8(a, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq)
 {
     if (B < 0 || Hq < 1 || Nq < 0) return 0;

@@ -34,6 +34,15 @@ struct DecodeArgs {
     int block_size, max_blocks, num_blocks;
 };
 
+struct Fp8FwdArgs {
+    const void *q, *k, *v;  // OCP e4m3 (E4M3FN) bytes
+    void *o;                // bf16
+    float *lse;
+    int B, Hq, Hkv, Nq, Nk, d;
+    float scale, v_scale;
+    int causal;
+};
+
 struct BwdArgs {
     const void *q, *k, *v, *o, *dout;
     const float *lse;
@@ -47,6 +56,7 @@ struct BwdArgs {
 // Each returns hipSuccess or the launch error.
 hipError_t launch_prefill_bf16(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_prefill_f32(const FwdArgs &a, hipStream_t stream);
+hipError_t launch_prefill_fp8(const Fp8FwdArgs &a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream);
 

@@ -1,0 +1,425 @@
+// prefill_fp8.hip -- fused attention forward for fp8 (OCP e4m3) q, k, v on
+// gfx950, bf16 output.
+//
+// The same computation as the bf16 kernel (one fused pass, online softmax,
+// the score matrix never leaves the chip: "Transformer 架构的数学与计算深度
+// 解析" sec. 6, "从注意力到 IO 感知执行" sec. 8 eqs. (1)-(2)), with inputs
+// stored as fp8 as FlashAttention-3 does on Hopper (pwwt.cn engineering
+// blog, sec. 4.4).  The same blog (sec. 7.2) warns that fp8 is sensitive to
+// quantisation: scores that lose precision before the softmax shift the
+// attention distribution.  This kernel therefore quantises nothing itself:
+//   * S^T = K Q^T runs on v_mfma_f32_32x32x64_f8f6f4.  The products of two
+//     e4m3 values are exact, but the instruction's internal sum keeps fewer
+//     bits than fp32: on gfx950 the 64-term dot products carry an absolute
+//     error of up to about 2^-16 of the largest result (measured), against
+//     2^-24 for the bf16 kernel's fp32 sums.  At scale 1/sqrt(d) that moves a
+//     scaled score by ~1e-4, well inside the bf16 tolerances; the error grows
+//     with |scale * score|, which is the sensitivity the blog warns about.
+//   * P^T stays bf16 (as in the bf16 kernel) and O^T = V^T P^T runs on the
+//     bf16 MFMA: each V tile arrives as fp8 and is converted once, exactly
+//     (every e4m3 value is a bf16 value), into a bf16 LDS tile by all 256
+//     threads (v_cvt_scalef32_pk_bf16_fp8, 16 conversions per thread per
+//     64-key tile at d = 128), one tile ahead of its use.
+// The caller folds the dequantisation factors of q and k into `scale`; the
+// factor of v multiplies the output (`v_scale`, applied in fp32 before the
+// final rounding).
+//
+// gfx950 mapping (as the bf16 kernel unless stated):
+//   * 4 waves x 32 query rows, BN = 64 keys per tile, two workgroups per CU.
+//   * Q^T (fp8, 32 bytes per lane per 64-wide k-step) stays in registers.
+//   * K tiles: fp8 rows of d bytes, HBM -> LDS by DMA two tiles ahead; the
+//     16-byte chunks are XOR-swizzled by the row so that the operand reads
+//     (32 rows x one chunk) are conflict-free.
+//   * V tiles: fp8 staging ring filled by DMA two tiles ahead, converted to
+//     the bf16 ring one tile ahead; P V reads it transposed
+//     (ds_read_b64_tr_b16) exactly as the bf16 kernel does.
+#include "kernels.h"
+
+#include <math.h>
+
+namespace attn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int BM = 128;
+constexpr int BN = 64;
+constexpr int NTHR = 256;
+constexpr float LN2 = 0.69314718055994530942f;
+constexpr float LOG2E = 1.44269504088896340736f;
+constexpr float RESCALE_SUM = 16777216.f;  // see the bf16 kernel
+constexpr int E8M0_ONE = 127;              // unit block scale of the f8f6f4 MFMA
+
+template <int D>
+struct Cfg {
+    static constexpr int CH8 = D / 16;            // 16-byte chunks of an fp8 row
+    static constexpr int KS8 = D / 64;            // k-steps of the fp8 score MFMA
+    static constexpr int CB = D / 32;             // 32-column blocks of O^T
+    static constexpr int RPW8 = 64 / CH8;         // fp8 rows one wave-wide DMA covers
+    static constexpr int ROUNDS8 = BN / (4 * RPW8);
+    static constexpr int TILE8 = BN * D;          // bytes of an fp8 tile
+    static constexpr int TILE16 = BN * D;         // elements of a bf16 tile
+    static constexpr int EPT = BN * D / NTHR;     // V elements each thread converts
+    static_assert(ROUNDS8 * 4 * RPW8 == BN, "tile split");
+    static_assert(EPT % 16 == 0, "whole 16-byte fp8 chunks per thread");
+};
+
+// Chunk swizzle of an fp8 K row (d bytes): 16 consecutive rows reading one
+// chunk hit 16 different 16-byte bank slots (rows of 128 B pair up in a
+// 256-byte bank line at d = 128, rows of 64 B group by four at d = 64).
+template <int D> __device__ __forceinline__ int swz8(int row);
+template <> __device__ __forceinline__ int swz8<128>(int row) { return (row >> 1) & 7; }
+template <> __device__ __forceinline__ int swz8<64>(int row) { return (row >> 2) & 3; }
+// Chunk swizzle of the bf16 V tile (as the bf16 kernel's V tile).
+template <int D> __device__ __forceinline__ int swz_v(int row);
+template <> __device__ __forceinline__ int swz_v<128>(int row) { return (row & 3) << 2; }
+template <> __device__ __forceinline__ int swz_v<64>(int row) { return (row & 2) << 1; }
+
+__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, E8M0_ONE, 0, E8M0_ONE);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(NTHR, 2) void prefill_fp8_kernel(
+    const uint8_t *__restrict__ Q, const uint8_t *__restrict__ K, const uint8_t *__restrict__ V,
+    __bf16 *__restrict__ O, float *__restrict__ LSE, int Hq, int Hkv, int Nq, int Nk, float sl2, float v_scale,
+    int n_qtiles, int total)
+{
+    using C = Cfg<D>;
+    __shared__ __attribute__((aligned(1024))) uint8_t sK0[C::TILE8];
+    __shared__ __attribute__((aligned(1024))) uint8_t sK1[C::TILE8];
+    __shared__ __attribute__((aligned(1024))) uint8_t sW0[C::TILE8];  // fp8 V staging
+    __shared__ __attribute__((aligned(1024))) uint8_t sW1[C::TILE8];
+    __shared__ __attribute__((aligned(1024))) __bf16 sV0[C::TILE16];  // bf16 V
+    __shared__ __attribute__((aligned(1024))) __bf16 sV1[C::TILE16];
+
+    // ---- work item (same order and XCD remap as the bf16 kernel) ----------
+    const int L = blockIdx.x;
+    const int xcd = L & 7, local = L >> 3;
+    const int per = total >> 3, rem = total & 7;
+    const int w = xcd * per + (xcd < rem ? xcd : rem) + local;
+    const int G = Hq / Hkv;
+    const int gq = w % G;
+    int t = w / G;
+    const int tq_ord = t % n_qtiles;
+    t /= n_qtiles;
+    const int hk = t % Hkv;
+    const int b = t / Hkv;
+    const int h = hk * G + gq;
+    const int tq = CAUSAL ? (n_qtiles - 1 - tq_ord) : tq_ord;
+    const int q0 = tq * BM;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 31, g = lane >> 5;
+    const int off = Nk - Nq;
+
+    const uint8_t *Qh = Q + ((size_t)(b * Hq + h) * Nq) * D;
+    const uint8_t *Kh = K + ((size_t)(b * Hkv + hk) * Nk) * D;
+    const uint8_t *Vh = V + ((size_t)(b * Hkv + hk) * Nk) * D;
+
+    // ---- Q^T operands: lane (n, g) holds d = 64 s + 32 g .. + 31 of row qi
+    const int qi = q0 + wave * 32 + n;
+    i32x8 qf[C::KS8];
+    if (qi < Nq) {
+        const i32x8 *src = reinterpret_cast<const i32x8 *>(Qh + (size_t)qi * D + 32 * g);
+#pragma unroll
+        for (int s = 0; s < C::KS8; ++s) qf[s] = src[2 * s];
+    } else {
+#pragma unroll
+        for (int s = 0; s < C::KS8; ++s) qf[s] = i32x8{};
+    }
+    // positive factor only (see the bf16 kernel): a negative scale negates Q
+    // (the e4m3 sign bit), zero becomes 1e-30
+    if (sl2 < 0.f) {
+        sl2 = -sl2;
+#pragma unroll
+        for (int s = 0; s < C::KS8; ++s) qf[s] ^= (int)0x80808080;
+    }
+    sl2 = sl2 < 1e-30f ? 1e-30f : sl2;
+
+    int kv_end = Nk;
+    if (CAUSAL) {
+        const int last_row = (q0 + BM < Nq ? q0 + BM : Nq);
+        const int e = last_row + off;
+        kv_end = e < Nk ? e : Nk;
+    }
+    const int ntiles = (kv_end + BN - 1) / BN;
+    const int lim = CAUSAL ? ((qi + off) < (Nk - 1) ? (qi + off) : (Nk - 1)) : (Nk - 1);
+    const int wave_first_row = q0 + wave * 32;
+
+    // ---- DMA lane offsets ----------------------------------------------------
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int ld_row = wave * C::RPW8 + lane / C::CH8, ld_slot = lane % C::CH8;
+    const int voff_k = ld_row * D + ((ld_slot ^ swz8<D>(ld_row)) * 16);
+    const int voff_w = ld_row * D + ld_slot * 16;  // staging: plain row-major
+    // BN fp8 rows base[row0 ..] into an LDS tile; rows past Nk read as 0
+    // (the descriptor ends at the last row)
+    // (the round stride is a named constant: this host compiler drops the
+    // kernel's host stub when the DMA builtin's soffset is written out as a
+    // product of template-dependent members inside the lambda)
+    constexpr int ROUND8 = 4 * C::RPW8 * D;
+    auto dma_rows8 = [&](const uint8_t *base, int row0, uint8_t *dst, int voff) {
+        const int left = Nk - row0;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(base + (size_t)row0 * D), (short)0, (left < BN ? left : BN) * D, 0x00020000);
+#pragma unroll
+        for (int r = 0; r < C::ROUNDS8; ++r) {
+            uint8_t *d = dst + (r * 4 + wave_s) * C::RPW8 * D;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)d, 16, voff, r * ROUND8, 0, 0);
+        }
+    };
+
+    // ---- V conversion (fp8 staging -> swizzled bf16 tile) ---------------------
+    // thread tid converts row tid / (NTHR / BN), elements cv_e0 .. + EPT - 1
+    constexpr int TPR = NTHR / BN;  // threads per row
+    const int cv_row = tid / TPR, cv_e0 = (tid % TPR) * C::EPT;
+    auto convert = [&](const uint8_t *src, __bf16 *dst) {
+#pragma unroll
+        for (int c8 = 0; c8 < C::EPT / 16; ++c8) {
+            const u32x4 x = *reinterpret_cast<const u32x4 *>(src + cv_row * D + cv_e0 + 16 * c8);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                u32x4 y;
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const uint32_t word = x[2 * half + i];
+                    y[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false));
+                    y[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true));
+                }
+                const int chunk = (cv_e0 + 16 * c8 + 8 * half) >> 3;  // bf16 chunk of 8 elements
+                *reinterpret_cast<u32x4 *>(dst + cv_row * D + ((chunk ^ swz_v<D>(cv_row)) * 8)) = y;
+            }
+        }
+    };
+
+    // ---- running state -----------------------------------------------------
+    f32x16 acc[C::CB];
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb) acc[cb] = f32x16{};
+    float m_ref = -INFINITY;
+    float l_run = 0.f;
+
+    const int tr_grp = lane >> 4, tr_j = lane & 15;
+    const int tr_key = 4 * (tr_grp >> 1) + (tr_j >> 2);
+    const int tr_col = 16 * (tr_grp & 1) + 4 * (tr_j & 3);
+    // K operand: row n (+32 for the second key half, same swizzle), bytes
+    // 64 s + 32 g .. + 31 = chunks 4 s + 2 g and 4 s + 2 g + 1
+    int k_off[C::KS8][2];
+#pragma unroll
+    for (int s = 0; s < C::KS8; ++s)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) k_off[s][hf] = n * D + (((4 * s + 2 * g + hf) ^ swz8<D>(n)) * 16);
+    int v_off[C::CB];
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb) {
+        const int col = cb * 32 + tr_col;
+        v_off[cb] = tr_key * D + (((col >> 3) ^ swz_v<D>(tr_key)) * 8) + (col & 7);
+    }
+
+    auto kfrag = [&](const uint8_t *sk, int kt, int s) {
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(sk + kt * 32 * D + k_off[s][0]);
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(sk + kt * 32 * D + k_off[s][1]);
+        return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto vfrag = [&](const __bf16 *sv, int cb, int kt, int hh) {
+        i16x4 part[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const __bf16 *p = sv + (kt * 32 + 16 * hh + 8 * half) * D + v_off[cb];
+            part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+        }
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto qk = [&](const uint8_t *sk, f32x16 (&st)[2]) {
+        st[0] = f32x16{};
+        st[1] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < C::KS8; ++s)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) st[kt] = mfma8(kfrag(sk, kt, s), qf[s], st[kt]);
+    };
+
+    // Rings: K[j] in sK[j & 1], fp8 V[j] in sW[j & 1] (both DMA'd two tiles
+    // ahead), bf16 V[j] in sV[j & 1] (converted one tile ahead).  Iteration j
+    // starts K[j+2], W[j+2], converts W[j+1] -> V[j+1], computes the scores of
+    // tile j+1 with the softmax of tile j, then P V of tile j.
+    auto kbuf = [&](int j) { return (j & 1) ? sK1 : sK0; };
+    auto wbuf = [&](int j) { return (j & 1) ? sW1 : sW0; };
+    auto vbuf = [&](int j) { return (j & 1) ? sV1 : sV0; };
+    auto dma = [&](int j) {
+        dma_rows8(Kh, j * BN, kbuf(j), voff_k);
+        dma_rows8(Vh, j * BN, wbuf(j), voff_w);
+    };
+
+    auto iteration = [&](const int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+        const int j0 = j * BN;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K[j+1], W[j+1] have landed
+        __syncthreads();                                   // ... for every wave; tile j-1 is free
+        if (j + 2 < ntiles) dma(j + 2);
+        if (j + 1 < ntiles) convert(wbuf(j + 1), vbuf(j + 1));
+        if (CAUSAL && j0 > wave_first_row + 31 + off) return;
+
+        const bool need_mask = (j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > wave_first_row + off);
+        if (need_mask) {
+            const int rel = lim - j0 - 4 * g;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kk = kt * 32 + 8 * (r >> 2) + (r & 3);
+                    if (kk > rel) cur[kt][r] = -INFINITY;
+                }
+            }
+        }
+        // scores of tile j+1 (2 * KS8 fp8 MFMAs) interleaved with P of tile j
+        const uint8_t *skn = kbuf(j + 1);
+        constexpr int NQK = 2 * C::KS8;
+        constexpr int PAIRS_PER = 16 / NQK;
+        u32x4 pb[2][2];
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};
+        const bool fresh = __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) != 0;
+        const float m_use = fresh ? 0.f : m_ref;
+        nxt[0] = f32x16{};
+        nxt[1] = f32x16{};
+        i32x8 kq = kfrag(skn, 0, 0);
+#pragma unroll
+        for (int i = 0; i < NQK; ++i) {
+            const int s = i >> 1, kt = i & 1;
+            const i32x8 cur_k = kq;
+            if (i + 1 < NQK) kq = kfrag(skn, (i + 1) & 1, (i + 1) >> 1);
+            nxt[kt] = mfma8(cur_k, qf[s], nxt[kt]);
+#pragma unroll
+            for (int q = 0; q < PAIRS_PER; ++q) {
+                const int pi = i * PAIRS_PER + q;
+                const int pkt = pi >> 3, hh = (pi >> 2) & 1, ii = pi & 3;
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[pkt][8 * hh + 2 * ii], sl2, -m_use));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[pkt][8 * hh + 2 * ii + 1], sl2, -m_use));
+                pb[pkt][hh][ii] = pack_bf16(p0, p1);
+                ps[ii] += p0 + p1;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        if (fresh || __builtin_amdgcn_ballot_w64(!(psum <= RESCALE_SUM)) != 0) {
+            float mr = cur[0][0];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = (kt == 0 ? 1 : 0); r < 16; ++r) mr = fmaxf(mr, cur[kt][r]);
+            const float mloc = mr * sl2;
+            const float mp = fmaxf(mloc, wave_xor32(mloc));
+            const float m_new = fmaxf(m_ref, mp);
+            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb) acc[cb] *= alpha;
+            m_ref = m_new;
+            const float mu = (m_ref == -INFINITY) ? 0.f : m_ref;
+            psum = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) {
+                        const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[kt][8 * hh + 2 * ii], sl2, -mu));
+                        const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[kt][8 * hh + 2 * ii + 1], sl2, -mu));
+                        pb[kt][hh][ii] = pack_bf16(p0, p1);
+                        psum += p0 + p1;
+                    }
+        }
+        l_run += psum;
+
+        // O^T += V^T P^T for tile j (bf16 V tile)
+        const __bf16 *svc = vbuf(j);
+        constexpr int NPV = 4 * C::CB;
+        constexpr int VAHEAD = 4;
+        bf16x8 vq[NPV];
+#pragma unroll
+        for (int i = 0; i < VAHEAD; ++i) vq[i] = vfrag(svc, i % C::CB, (i / C::CB) >> 1, (i / C::CB) & 1);
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+            const int cb = i % C::CB, kh = i / C::CB, kt = kh >> 1, hh = kh & 1;
+            if (i + VAHEAD < NPV) {
+                const int i2 = i + VAHEAD;
+                const int kh2 = i2 / C::CB;
+                vq[i2] = vfrag(svc, i2 % C::CB, kh2 >> 1, kh2 & 1);
+            }
+            acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[i], __builtin_bit_cast(bf16x8, pb[kt][hh]), acc[cb],
+                                                              0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    f32x16 stA[2], stB[2];
+    if (ntiles > 0) {
+        dma(0);
+        if (ntiles > 1) dma(1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        convert(wbuf(0), vbuf(0));
+        qk(sK0, stA);
+    }
+    for (int j = 0; j < ntiles; j += 2) {
+        iteration(j, stA, stB);
+        if (j + 1 < ntiles) iteration(j + 1, stB, stA);
+    }
+
+    // ---- epilogue ------------------------------------------------------------
+    const float l_tot = l_run + wave_xor32(l_run);
+    if (qi < Nq) {
+        const float inv = l_tot > 0.f ? v_scale / l_tot : 0.f;
+        __bf16 *orow = O + ((size_t)(b * Hq + h) * Nq + qi) * D;
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int c = cb * 32 + 8 * rr + 4 * g;
+                const uint32_t lo = pack_bf16(acc[cb][4 * rr + 0] * inv, acc[cb][4 * rr + 1] * inv);
+                const uint32_t hi = pack_bf16(acc[cb][4 * rr + 2] * inv, acc[cb][4 * rr + 3] * inv);
+                *reinterpret_cast<u32x2 *>(orow + c) = u32x2{lo, hi};
+            }
+        }
+        if (LSE && g == 0)
+            LSE[(size_t)(b * Hq + h) * Nq + qi] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * LN2 : -INFINITY;
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const Fp8FwdArgs &a, hipStream_t stream) {
+    const float sl2 = a.scale * LOG2E;
+    const int n_qtiles = (a.Nq + BM - 1) / BM;
+    const long long total = (long long)a.B * a.Hq * n_qtiles;
+    if (total <= 0) return hipSuccess;
+    if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((prefill_fp8_kernel<D, CAUSAL>), dim3((unsigned)total), dim3(NTHR), 0, stream,
+                       (const uint8_t *)a.q, (const uint8_t *)a.k, (const uint8_t *)a.v, (__bf16 *)a.o, a.lse,
+                       a.Hq, a.Hkv, a.Nq, a.Nk, sl2, a.v_scale, n_qtiles, (int)total);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_fp8(const Fp8FwdArgs &a, hipStream_t stream) {
+    if (a.d == 128) return a.causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
+    return a.causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
+}
+
+}  // namespace attn

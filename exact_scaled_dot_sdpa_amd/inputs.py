@@ -2,7 +2,7 @@
 
 This module holds no attention arithmetic.  It only draws iid N(0, 1) values
 from a seeded CPU ``torch.Generator`` (in fp32, then rounded to nearest even to
-the workload's element type) and describes the workload shapes.  The HIP path
+the workload's element type: fp32, bf16 or fp8 e4m3) and describes the workload shapes.  The HIP path
 and the oracle consume the very same rounded values.
 
 Draw order is fixed: q, k, v for prefill (then do for the backward pass);
@@ -14,7 +14,7 @@ from typing import Optional
 
 import torch
 
-DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
 
 
 @dataclass(frozen=True)

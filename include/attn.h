@@ -86,6 +86,35 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
              int causal, int dtype, hipStream_t stream);
 
 /*
+ * attn_fwd_fp8 -- attn_fwd for q, k, v stored as fp8 (OCP e4m3, E4M3FN: 1
+ * sign, 4 exponent, 3 mantissa bits, bias 7, no infinities), output bf16.
+ *
+ * FlashAttention-3 uses fp8 on Hopper (pwwt.cn engineering blog on
+ * Transformer algorithm evolution, sec. 4.4); the same blog (sec. 7.2) warns
+ * that fp8 is sensitive to quantisation, because scores that lose precision
+ * before the softmax shift the attention distribution.  This call quantises
+ * nothing beyond its inputs: the weights enter P V in bf16 as in attn_fwd and
+ * V is widened to bf16 exactly.  The scores come from the fp8 matrix
+ * instruction, whose products are exact but whose internal sums keep about
+ * 16 significant bits (an absolute error up to ~2^-16 of the largest
+ * 64-term dot product, measured on gfx950) instead of fp32's 24.  At
+ * scale = 1/sqrt(d) the results meet attn_fwd's bf16 tolerances; the score
+ * error grows with |scale * q.k|.
+ *
+ *   q [B, Hq, Nq, d], k / v [B, Hkv, Nk, d]   e4m3 bytes (read)
+ *   o [B, Hq, Nq, d] bf16 (written), lse [B, Hq, Nq] fp32 or NULL
+ *
+ * O = v_scale * softmax(scale * Q K^T [+ causal mask]) V, where Q, K, V are
+ * the stored e4m3 values: a caller holding fp8 tensors with dequantisation
+ * factors sq, sk, sv passes scale = softmax_scale * sq * sk and v_scale = sv.
+ * lse is that of the scaled scores.  Sizes, head mapping, causal alignment,
+ * returns and errors as attn_fwd (v_scale must be finite).
+ */
+int attn_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+                 int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                 float v_scale, int causal, hipStream_t stream);
+
+/*
  * attn_bwd_workspace_bytes -- bytes of device workspace attn_bwd needs:
  * two fp32 per query row (B * Hq * Nq * 8).  Returns 0 for invalid sizes.
  */

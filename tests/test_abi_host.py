@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert names == sorted(["attn_fwd", "attn_decode", "attn_decode_paged", "attn_decode_workspace_bytes",
-                            "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str"])
+                            "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_fp8", "attn_status_str"])
     lib = ctypes.CDLL(E.lib_path())
     for n in names:
         assert hasattr(lib, n), "libattn.so does not export %s" % n
@@ -202,3 +202,25 @@ def test_bwd_workspace_bytes():
     assert E.attn_bwd_workspace_bytes(0, 8, 100) == 0
     assert E.attn_bwd_workspace_bytes(1, 0, 100) == 0
     assert E.attn_bwd_workspace_bytes(1, 4, -1) == 0
+
+
+def fwd8(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=128, scale=0.09, v_scale=1.0, causal=0):
+    return E.lib().attn_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, v_scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=3, Hkv=2), E.ATTN_ERR_INVALID_ARG),
+    (dict(Nk=-1), E.ATTN_ERR_INVALID_ARG),
+    (dict(causal=1, Nq=9), E.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), E.ATTN_ERR_INVALID_ARG),
+    (dict(v_scale=float("nan")), E.ATTN_ERR_INVALID_ARG),
+    (dict(d=80), E.ATTN_ERR_UNSUPPORTED),
+    (dict(q=None), E.ATTN_ERR_INVALID_ARG),
+    (dict(v=None), E.ATTN_ERR_INVALID_ARG),
+    (dict(k=P + 8), E.ATTN_ERR_INVALID_ARG),
+    (dict(lse=P + 1), E.ATTN_ERR_INVALID_ARG),
+    (dict(B=0), E.ATTN_OK),
+    (dict(Nq=0), E.ATTN_OK),
+])
+def test_fwd_fp8_validation(kw, status):
+    assert fwd8(**kw) == status
