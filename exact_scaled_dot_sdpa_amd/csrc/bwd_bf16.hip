@@ -298,21 +298,22 @@ __global__ __launch_bounds__(NTHR, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb) acc[cb] = f32x16{};
 
-    auto kbuf = [&](int j) { return (j & 1) ? sK1 : sK0; };
-    auto vbuf = [&](int j) { return (j & 1) ? sV1 : sV0; };
-    auto load = [&](int j) {
-        dma_tile<D, BN, 4>(Kh, j * BN, Nk, kbuf(j), voff_k, wave_s);
-        dma_tile<D, BN, 4>(Vh, j * BN, Nk, vbuf(j), voff_v, wave_s);
+    auto load = [&](int j, __bf16 *k_dst, __bf16 *v_dst) {
+        dma_tile<D, BN, 4>(Kh, j * BN, Nk, k_dst, voff_k, wave_s);
+        dma_tile<D, BN, 4>(Vh, j * BN, Nk, v_dst, voff_v, wave_s);
     };
 
-    if (ntiles > 0) load(0);
-    for (int j = 0; j < ntiles; ++j) {
+    if (ntiles > 0) load(0, sK0, sV0);
+    // Tile j reads one stage and refills the other with tile j+1.  The loop
+    // below names the stage arrays explicitly (even tiles stage 0, odd tiles
+    // stage 1): with a run-time choice the compiler cannot tell the stages
+    // apart and waits for the just-issued refill before the tile's reads.
+    auto tile = [&](int j, const __bf16 *sk, const __bf16 *sv, __bf16 *nk, __bf16 *nv) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (j + 1 < ntiles) load(j + 1);
+        if (j + 1 < ntiles) load(j + 1, nk, nv);
         const int j0 = j * BN;
-        if (CAUSAL && j0 > wave_first_row + 31 + off) continue;  // no row of this wave sees tile j
-        const __bf16 *sk = kbuf(j), *sv = vbuf(j);
+        if (CAUSAL && j0 > wave_first_row + 31 + off) return;  // no row of this wave sees tile j
 
         // one 32-key half at a time: S^T = K Q^T, dP^T = V dO^T, then P^T and
         // dS^T = P^T (dP^T - D) for this lane's row (lane (n, g) holds keys
@@ -345,6 +346,10 @@ __global__ __launch_bounds__(NTHR, 2) void bwd_dq_kernel(
                 for (int cb = 0; cb < C::CB; ++cb) acc[cb] = mfma(tr_frag<D>(sk, kt_off, cb, 2 * kt + hh), bs, acc[cb]);
             }
         }
+    };
+    for (int j = 0; j < ntiles; j += 2) {
+        tile(j, sK0, sV0, sK1, sV1);
+        if (j + 1 < ntiles) tile(j + 1, sK1, sV1, sK0, sV0);
     }
 
     // dQ = scale * acc; lane (n, g) holds columns cb*32 + 8 rr + 4 g + 0..3
