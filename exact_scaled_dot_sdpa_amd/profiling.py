@@ -26,6 +26,7 @@ KERNELS = {
     "prefill": ["prefill_bf16_kernel"],
     "decode": ["decode_chunk_kernel", "decode_merge_kernel"],
     "bwd": ["bwd_pre_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel"],
+    "fp8": ["prefill_fp8_kernel"],
 }
 COPY_KERNEL = "copyBuffer"
 
