@@ -2,7 +2,7 @@
 """Benchmark of the attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-paged] [--no-rect]
-                    [--no-bwd] [--no-fp8]
+                    [--no-bwd] [--no-fp8] [--no-configs]
 
 One step is one pass of the whole path over synthetic inputs already resident
 in device memory:
@@ -28,7 +28,9 @@ forward's o and lse and a seeded upstream gradient, counting 2.5x the forward
 FLOPs (five matrix products per visible pair); `fp8_prefill` times
 attn_fwd_fp8 on the prefill workload's shape with e4m3 inputs (scores on the
 fp8 MFMA, P V on the bf16 MFMA; its peak is the 3.33 PFLOP/s that half the
-FLOPs at 5.0 and half at 2.5 PFLOP/s allow).
+FLOPs at 5.0 and half at 2.5 PFLOP/s allow); `other_configs` times attn_fwd
+on the smaller prefill shapes (C1 fp32, C2a/C2b GPT-2-small-sized, C3a/C3a'/C3b)
+once each, for context: they are parity cases and too small to fill the chip.
 """
 import argparse
 import json
@@ -62,6 +64,7 @@ def parse():
     ap.add_argument("--paged-block-size", type=int, default=64)
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 prefill measurement")
+    ap.add_argument("--no-configs", action="store_true", help="skip the smaller prefill configs")
     ap.add_argument("--no-rect", action="store_true",
                     help="skip the chunked-prefill and cross-attention measurements")
     return ap.parse_args()
@@ -186,6 +189,40 @@ def fp8_prefill_line(E, A, I, dev, steps=20, warmup=50):
                     "with V widened exactly; bf16 output"}
 
 
+def other_configs_line(E, A, I, dev, steps=20, warmup=20):
+    """attn_fwd on the smaller prefill shapes, each timed on its own."""
+    import torch
+
+    out = {}
+    for name, causal in (("C1", False), ("C2a", False), ("C2b", True), ("C3a", True), ("C3a'", True),
+                         ("C3b", True)):
+        w = I.WORKLOADS[name]
+        q, k, v = (t.to(dev) for t in I.workload_inputs(name))
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        ms = timed_ms(lambda i: E.attn_fwd(q, k, v, scale=w.scale, causal=causal, o=o, lse=lse), steps, warmup)
+        fl = A.prefill_flops(w.B, w.Hq, w.Nq, w.Nkv, w.d, causal)
+        by = A.prefill_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.d, w.dtype)
+        tf = fl / (ms * 1e-3) / 1e12
+        out[name] = {"shape": "%s B%d H%d N%d d%d %s" % (w.dtype, w.B, w.Hq, w.Nq, w.d,
+                                                         "causal" if causal else "full"),
+                     "us": round(ms * 1e3, 2), "tflops": round(tf, 2),
+                     "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4) if w.dtype == "bf16" else None,
+                     "gbs": round(by / (ms * 1e-3) / 1e9, 1)}
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(q, k, v, w, target_s):
     """The oracle, as it stands, on a bounded sample of prefill rows."""
     import numpy as np
@@ -222,6 +259,7 @@ def cpu_baseline(q, k, v, w, target_s):
         "value": f / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": nthreads,
+        "cpu": cpu_model(),
         "kind": "oracle",
         "sample": "%d random (head, row) pairs of the GQA causal prefill workload (%.3g GFLOP of the "
                   "%.4g GFLOP total), fp64, %.1f s; calibration rate %.3g GFLOP/s"
@@ -371,6 +409,8 @@ def main():
         out["backward"] = backward_line(E, A, I, dev, q, k, v, o, lse, wp)
     if run_8:
         out["fp8_prefill"] = fp8_prefill_line(E, A, I, dev)
+    if run_p and not args.no_configs:
+        out["other_configs"] = other_configs_line(E, A, I, dev)
     if run_p and not args.no_rect:
         out["chunked_prefill"] = rect_prefill_line(E, A, I, dev, "X1")
         out["cross_attention"] = rect_prefill_line(E, A, I, dev, "X2")

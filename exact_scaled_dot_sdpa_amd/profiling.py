@@ -14,10 +14,10 @@ exactly that many bytes.  The JSON records each kernel's source digest;
 bench.py reports a kernel's bytes only while its sources are unchanged.
 """
 import argparse
-import re
 import csv
 import json
 import os
+import re
 import statistics
 import sys
 
@@ -154,6 +154,58 @@ def traffic(fetch_csv, write_csv, calib_mib, cmd_fetch, cmd_write, json_out, out
     return text
 
 
+# Normalisations of the SQ counters on MI355X: SQ_CYCLES sums the cycles of
+# every shader engine (8 XCDs x 4), SQ_VALU_MFMA_BUSY_CYCLES the busy cycles of
+# every SIMD (256 CUs x 4), the SQ_WAVE/WAIT/BUSY counters count in units of
+# four cycles per wave, and one MFMA MOP is 512 FLOPs.
+N_SE, N_SIMD, MOP_FLOPS = 32, 1024, 512
+
+
+def counters(csv_path, cmd, out, algorithmic=None):
+    """Per-kernel medians over the dispatches of a --pmc run, with the derived
+    figures: executed MFMA FLOPs against the algorithmic ones, the clock
+    (cycles over duration), the share of SIMD cycles with the MFMA unit busy,
+    and the shares of wave time spent waiting."""
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        k = _short(r["Kernel_Name"])
+        d = per.setdefault(k, {}).setdefault(r["Dispatch_Id"], {"dur": int(r["End_Timestamp"]) -
+                                                               int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    lines = ["# rocprofv3 SQ counters", "", "Command:", "", "```", cmd, "```", "",
+             "Medians over the dispatches of each kernel. The derived columns assume MI355X's 32 shader "
+             "engines (SQ_CYCLES sums them) and 1024 SIMDs (SQ_VALU_MFMA_BUSY_CYCLES sums them); wave "
+             "counters tick every 4 cycles; one MFMA MOP is 512 FLOPs.", ""]
+    names = sorted({c for k in per.values() for d in k.values() for c in d if c != "dur"})
+    lines.append("| kernel | dispatches | " + " | ".join(names) + " |")
+    lines.append("|---|---|" + "---|" * len(names))
+    derived = ["", "| kernel | duration (us) | clock (GHz) | MFMA busy | executed MFMA TFLOP | algorithmic TFLOP |"
+               " wait share | wait-issue share |", "|---|---|---|---|---|---|---|---|"]
+    for k, ds in per.items():
+        if k.startswith("__amd"):
+            continue
+        med = {c: statistics.median(d[c] for d in ds.values() if c in d) for c in names if
+               any(c in d for d in ds.values())}
+        dur = statistics.median(d["dur"] for d in ds.values())
+        lines.append("| %s | %d | " % (k, len(ds)) + " | ".join("%.4g" % med[c] if c in med else "" for c in names)
+                     + " |")
+        cyc = med.get("SQ_CYCLES", 0.0) / N_SE
+        clock = cyc / dur if dur > 0 else 0.0  # cycles per ns = GHz
+        busy = med.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (N_SIMD * cyc) if cyc > 0 else 0.0
+        mops = sum(v for c, v in med.items() if c.startswith("SQ_INSTS_VALU_MFMA_MOPS"))
+        wc = med.get("SQ_WAVE_CYCLES", 0.0)
+        alg = (algorithmic or {}).get(k)
+        derived.append("| %s | %.1f | %.2f | %s | %s | %s | %s | %s |" % (
+            k, dur / 1e3, clock, "%.1f%%" % (100 * busy) if busy else "",
+            "%.4g" % (mops * MOP_FLOPS / 1e12) if mops else "", "%.4g" % (alg / 1e12) if alg else "",
+            "%.1f%%" % (100 * med["SQ_WAIT_ANY"] / wc) if wc and "SQ_WAIT_ANY" in med else "",
+            "%.1f%%" % (100 * med["SQ_WAIT_INST_ANY"] / wc) if wc and "SQ_WAIT_INST_ANY" in med else ""))
+    text = "\n".join(lines + derived) + "\n"
+    with open(out, "w") as f:
+        f.write(text)
+    return text
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -171,9 +223,21 @@ def main(argv=None):
     t.add_argument("--cmd-write", required=True)
     t.add_argument("--json", required=True)
     t.add_argument("--out", required=True)
+    c = sub.add_parser("counters", help="summarise an SQ counter run")
+    c.add_argument("csv")
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--out", required=True)
+    c.add_argument("--algorithmic", default=None,
+                   help="kernel=FLOPs[,kernel=FLOPs...]: algorithmic FLOPs per launch to compare with")
     a = ap.parse_args(argv)
     if a.what == "stats":
         print(stats(a.csv, a.cmd, a.out, a.trace, a.last))
+    elif a.what == "counters":
+        alg = {}
+        for item in (a.algorithmic.split(",") if a.algorithmic else []):
+            k, v = item.split("=")
+            alg[k] = float(v)
+        print(counters(a.csv, a.cmd, a.out, alg))
     else:
         print(traffic(a.fetch, a.write, a.calib_mib, a.cmd_fetch, a.cmd_write, a.json, a.out))
 
