@@ -28,9 +28,9 @@
 //     K tile with ds_read_b64_tr_b16.  Two workgroups per CU (two waves per
 //     SIMD), so one wave's exp / VALU work hides behind another's MFMAs.
 //   * bwd_dkdv_kernel: a workgroup of 8 waves owns 128 keys of one K/V head;
-//     K^T (registers) and V^T (LDS) stay resident while Q / dO tiles of 64 rows of every
+//     its K and V rows stay resident in LDS while Q / dO tiles of 64 rows of every
 //     query head of the GQA group stream through LDS, so dK and dV are summed
-//     over the group in registers (V's rows sit in LDS for the whole kernel
+//     over the group in registers (K and V sit in LDS for the whole kernel
 //     to leave room for that).  Two waves share each 32-key slice, one
 //     per 32-row half of a tile (two waves per SIMD again), and add their
 //     partial sums through LDS at the end.  Per half tile: S = Q K^T,
@@ -390,6 +390,7 @@ __global__ __launch_bounds__(KNW * 64) void bwd_dkdv_kernel(
     __shared__ __attribute__((aligned(256))) float sE0[BQ];
     __shared__ __attribute__((aligned(256))) float sE1[BQ];
     __shared__ __attribute__((aligned(1024))) __bf16 sV[BKN * D];  // the workgroup's V rows
+    __shared__ __attribute__((aligned(1024))) __bf16 sK[BKN * D];  // the workgroup's K rows
 
     // work item: (batch, KV head) outermost, then key tile (heaviest causal
     // tile, the first, first)
@@ -408,18 +409,9 @@ __global__ __launch_bounds__(KNW * 64) void bwd_dkdv_kernel(
     const int wk0 = k0 + kw * 32;  // this wave's first key
     const int kj = wk0 + n;        // this lane's key
 
-    // K^T operands in registers; V rows in LDS (registers are the limit at
-    // two waves per SIMD), both for the whole kernel
+    // K and V rows in LDS for the whole kernel (registers are the limit at
+    // two waves per SIMD)
     const size_t krow0 = (size_t)(b * Hkv + hk) * Nk;
-    bf16x8 kf[C::KS];
-    if (kj < Nk) {
-        const bf16x8 *sk = reinterpret_cast<const bf16x8 *>(K + (krow0 + kj) * D + 8 * g);
-#pragma unroll
-        for (int s = 0; s < C::KS; ++s) kf[s] = sk[2 * s];
-    } else {
-#pragma unroll
-        for (int s = 0; s < C::KS; ++s) kf[s] = bf16x8{};
-    }
 
     // query tiles that see some key of the workgroup: rows >= k0 - off
     const int n_qt = (Nq + BQ - 1) / BQ;
@@ -472,6 +464,7 @@ __global__ __launch_bounds__(KNW * 64) void bwd_dkdv_kernel(
 
     if (steps > 0) {
         dma_tile<D, BKN, KNW>(V + krow0 * D, k0, Nk, sV, voff_v, wave_s);
+        dma_tile<D, BKN, KNW>(K + krow0 * D, k0, Nk, sK, voff_v, wave_s);
         load(0);
     }
     for (int u = 0; u < steps; ++u) {
@@ -487,7 +480,8 @@ __global__ __launch_bounds__(KNW * 64) void bwd_dkdv_kernel(
         f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int s = 0; s < C::KS; ++s)
-            sc = mfma(*reinterpret_cast<const bf16x8 *>(sq + rq_base + (((2 * s) ^ x_rt) * 8)), kf[s], sc);
+            sc = mfma(*reinterpret_cast<const bf16x8 *>(sq + rq_base + (((2 * s) ^ x_rt) * 8)),
+                      *reinterpret_cast<const bf16x8 *>(sK + rv_base + (((2 * s) ^ x_rows) * 8)), sc);
 #pragma unroll
         for (int s = 0; s < C::KS; ++s)
             dp = mfma(*reinterpret_cast<const bf16x8 *>(sd + rq_base + (((2 * s) ^ x_rt) * 8)),
