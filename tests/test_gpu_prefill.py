@@ -60,6 +60,9 @@ RAGGED = [
     ("bf16", 128, 2, 64, 16, 1000, 1000, True),
     ("bf16", 64, 2, 128, 8, 700, 1100, True),    # chunked prefill
     ("bf16", 128, 1, 256, 32, 520, 300, False),  # cross-attention
+    # causal chunks with enough 256-row work items: the 8-wave kernel
+    ("bf16", 64, 2, 128, 16, 300, 1000, True),
+    ("bf16", 128, 2, 128, 16, 300, 700, True),
     ("f32", 64, 2, 2, 1, 100, 100, True),
     ("f32", 128, 1, 4, 2, 70, 130, True),
     ("f32", 128, 1, 2, 1, 33, 17, False),
@@ -145,6 +148,22 @@ def test_gqa_equals_repeated_mha(G):
     o1, l1 = gpu_fwd(q, k, v, 0.1, True)
     o2, l2 = gpu_fwd(q, k.repeat_interleave(G, dim=1), v.repeat_interleave(G, dim=1), 0.1, True)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("causal,Nq,Nk", [(False, 300, 520), (True, 300, 700)])
+def test_wide_and_narrow_workgroups_agree(causal, Nq, Nk):
+    """With many query heads, non-causal and chunked-causal launches use
+    256-row workgroups of 8 waves; one head alone is too small a grid for that
+    and uses 128-row workgroups of 4 waves.  Each row's arithmetic is the same
+    in both, so the outputs must agree bit for bit."""
+    B, Hq, Hkv, d = 2, 128, 16, 128
+    q, k, v = I.prefill_inputs(B, Hq, Hkv, Nq, Nk, d, "bf16", seed=61 + Nq)
+    o_all, l_all = gpu_fwd(q, k, v, 0.09, causal)
+    G = Hq // Hkv
+    for b, h in [(0, 0), (1, 37), (1, Hq - 1)]:
+        hk = h // G
+        o1, l1 = gpu_fwd(q[b:b + 1, h:h + 1], k[b:b + 1, hk:hk + 1], v[b:b + 1, hk:hk + 1], 0.09, causal)
+        assert np.array_equal(o1[0, 0], o_all[b, h]) and np.array_equal(l1[0, 0], l_all[b, h]), (b, h)
 
 
 def test_run_twice_bitwise():
