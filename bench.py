@@ -18,7 +18,8 @@ FLOPs: 4*d per visible query/key pair), the decode bandwidth in GB/s (valid
 cache rows plus q, o, lse) in `decode`, and for each kernel its roofline
 fraction from its average duration measured with HIP events on the stream the
 kernels run on.  `cpu_baseline` times the fp64 oracle on a bounded sample of the
-prefill rows on the host cores.  `decode_paged` times the decode workload
+prefill rows on the host cores, and (`per_config`) on each smaller prefill
+workload in full, next to that workload's GPU time.  `decode_paged` times the decode workload
 against a paged cache (block table over a shuffled pool) on its own, after the
 timed steps; `chunked_prefill` (a 2048-token chunk over 8192 cached tokens,
 causal bottom-right) and `cross_attention` (2048 queries over 4096 keys,
@@ -189,14 +190,18 @@ def fp8_prefill_line(E, A, I, dev, steps=20, warmup=50):
                     "with V widened exactly; bf16 output"}
 
 
+# the smaller prefill workloads, timed one by one (and, in the oracle's leg, run in full)
+OTHER_CONFIGS = ("C1", "C2a", "C2b", "C3a", "C3a'", "C3b")
+
+
 def other_configs_line(E, A, I, dev, steps=20, warmup=20):
     """attn_fwd on the smaller prefill shapes, each timed on its own."""
     import torch
 
     out = {}
-    for name, causal in (("C1", False), ("C2a", False), ("C2b", True), ("C3a", True), ("C3a'", True),
-                         ("C3b", True)):
+    for name in OTHER_CONFIGS:
         w = I.WORKLOADS[name]
+        causal = w.causal
         q, k, v = (t.to(dev) for t in I.workload_inputs(name))
         o = torch.empty_like(q)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
@@ -223,7 +228,7 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(q, k, v, w, target_s):
+def cpu_baseline(q, k, v, w, target_s, per_config=()):
     """The oracle, as it stands, on a bounded sample of prefill rows."""
     import numpy as np
 
@@ -255,7 +260,7 @@ def cpu_baseline(q, k, v, w, target_s):
     oracle.attn_rows(qd, kd, vd, w.scale, w.causal, rows, nthreads=nthreads)
     dt = time.perf_counter() - t0
     f = flops(rows)
-    return {
+    res = {
         "value": f / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": nthreads,
@@ -266,6 +271,21 @@ def cpu_baseline(q, k, v, w, target_s):
                   % (n, f / 1e9, 4.0 * w.d * w.Hq * w.N * (w.N + 1) / 2 / 1e9, dt, rate / 1e9),
         "seconds": dt,
     }
+    if per_config:
+        # the smaller prefill configs in full, for the oracle's wall time next
+        # to the GPU's (a few seconds together)
+        from exact_scaled_dot_sdpa_amd import accounting as A
+        per = {}
+        for name in per_config:
+            c = I.WORKLOADS[name]
+            cq, ck, cv = [I.to_f64(t) for t in I.workload_inputs(name)]
+            t0 = time.perf_counter()
+            oracle.attn(cq, ck, cv, c.scale, c.causal, nthreads=nthreads)
+            cdt = time.perf_counter() - t0
+            cf = A.prefill_flops(c.B, c.Hq, c.Nq, c.Nkv, c.d, c.causal)
+            per[name] = {"seconds": round(cdt, 4), "gflop": round(cf / 1e9, 3), "gflops": round(cf / cdt / 1e9, 1)}
+        res["per_config"] = per
+    return res
 
 
 def main():
@@ -415,7 +435,11 @@ def main():
         out["chunked_prefill"] = rect_prefill_line(E, A, I, dev, "X1")
         out["cross_attention"] = rect_prefill_line(E, A, I, dev, "X2")
     if not args.no_cpu_baseline and run_p:
-        out["cpu_baseline"] = cpu_baseline(q_cpu, k_cpu, v_cpu, wp, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(q_cpu, k_cpu, v_cpu, wp, args.cpu_seconds,
+                                           per_config=() if args.no_configs else OTHER_CONFIGS)
+        for name, rec in out["cpu_baseline"].get("per_config", {}).items():
+            if name in out.get("other_configs", {}):
+                rec["gpu_us"] = out["other_configs"][name]["us"]
     print(json.dumps(out), flush=True)
 
 
