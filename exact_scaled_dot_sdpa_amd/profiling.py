@@ -159,6 +159,8 @@ def traffic(fetch_csv, write_csv, calib_mib, cmd_fetch, cmd_write, json_out, out
 # every SIMD (256 CUs x 4), the SQ_WAVE/WAIT/BUSY counters count in units of
 # four cycles per wave, and one MFMA MOP is 512 FLOPs.
 N_SE, N_SIMD, MOP_FLOPS = 32, 1024, 512
+# MI355X dense MFMA peaks (TFLOP/s) and the engine clock they assume
+PEAK_BF16_TFLOPS, PEAK_FP8_TFLOPS, PEAK_CLOCK_GHZ = 2500.0, 5000.0, 2.4
 
 
 def counters(csv_path, cmd, out, algorithmic=None):
@@ -180,7 +182,8 @@ def counters(csv_path, cmd, out, algorithmic=None):
     lines.append("| kernel | dispatches | " + " | ".join(names) + " |")
     lines.append("|---|---|" + "---|" * len(names))
     derived = ["", "| kernel | duration (us) | clock (GHz) | MFMA busy | executed MFMA TFLOP | algorithmic TFLOP |"
-               " wait share | wait-issue share |", "|---|---|---|---|---|---|---|---|"]
+               " algorithmic rate vs peak at this clock | wait share | wait-issue share |",
+               "|---|---|---|---|---|---|---|---|---|"]
     for k, ds in per.items():
         if k.startswith("__amd"):
             continue
@@ -195,9 +198,16 @@ def counters(csv_path, cmd, out, algorithmic=None):
         mops = sum(v for c, v in med.items() if c.startswith("SQ_INSTS_VALU_MFMA_MOPS"))
         wc = med.get("SQ_WAVE_CYCLES", 0.0)
         alg = (algorithmic or {}).get(k)
-        derived.append("| %s | %.1f | %.2f | %s | %s | %s | %s | %s |" % (
+        # dense peak scaled to the measured clock; a kernel mixing fp8 and
+        # bf16 MFMAs gets the rate of its executed mix
+        vs_clock = ""
+        if alg and mops and clock > 0 and dur >= 100e3:  # the clock is only meaningful for long kernels
+            f8 = med.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0) / mops
+            peak = 1.0 / (f8 / PEAK_FP8_TFLOPS + (1.0 - f8) / PEAK_BF16_TFLOPS) * clock / PEAK_CLOCK_GHZ
+            vs_clock = "%.1f%% of %.0f TFLOP/s" % (100 * (alg / (dur * 1e-9) / 1e12) / peak, peak)
+        derived.append("| %s | %.1f | %.2f | %s | %s | %s | %s | %s | %s |" % (
             k, dur / 1e3, clock, "%.1f%%" % (100 * busy) if busy else "",
-            "%.4g" % (mops * MOP_FLOPS / 1e12) if mops else "", "%.4g" % (alg / 1e12) if alg else "",
+            "%.4g" % (mops * MOP_FLOPS / 1e12) if mops else "", "%.4g" % (alg / 1e12) if alg else "", vs_clock,
             "%.1f%%" % (100 * med["SQ_WAIT_ANY"] / wc) if wc and "SQ_WAIT_ANY" in med else "",
             "%.1f%%" % (100 * med["SQ_WAIT_INST_ANY"] / wc) if wc and "SQ_WAIT_INST_ANY" in med else ""))
     text = "\n".join(lines + derived) + "\n"
