@@ -51,6 +51,8 @@
 
 #include <math.h>
 
+#include <atomic>
+
 namespace attn {
 namespace {
 
@@ -645,19 +647,21 @@ template <int D, int QR, int NST>
 hipError_t launch_cfg(const DecodeArgs &a, hipStream_t stream) {
     int n_wg = a.n_wg;
     if (n_wg <= 0) {
-        // as many single-wave workgroups as the chip holds at once
-        static int cached[64];
+        // as many single-wave workgroups as the chip holds at once (queried
+        // once per device; concurrent first calls store the same value)
+        static std::atomic<int> cached[64];
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-        if (cached[dev] == 0) {
+        n_wg = cached[dev].load(std::memory_order_relaxed);
+        if (n_wg == 0) {
             int cus = 0, per_cu = 0;
             hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
             if (e != hipSuccess) return e;
             e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_chunk_kernel<D, QR, NST>, 64, 0);
             if (e != hipSuccess) return e;
-            cached[dev] = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+            n_wg = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+            cached[dev].store(n_wg, std::memory_order_relaxed);
         }
-        n_wg = cached[dev];
     }
     if (n_wg > a.max_wg) n_wg = a.max_wg;
     const float sl2 = a.scale * LOG2E;

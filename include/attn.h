@@ -19,8 +19,9 @@
  *
  * Conventions shared by every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
- *     allocates nothing and keeps no mutable global state; calls on different
- *     streams may run concurrently.
+ *     allocates nothing.  Its only global state is a per-device cache of device
+ *     properties (compute-unit count, decode occupancy), filled atomically on
+ *     first use; calls on different streams may run concurrently.
  *   - Tensors are contiguous, row-major, head dim innermost, 16-byte aligned
  *     (lse and seq_lens: 4-byte aligned).
  *   - Calls are asynchronous on `stream` (NULL = the null stream) and return
