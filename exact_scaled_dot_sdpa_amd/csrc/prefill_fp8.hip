@@ -16,10 +16,14 @@
 //     scaled score by ~1e-4, well inside the bf16 tolerances; the error grows
 //     with |scale * score|, which is the sensitivity the blog warns about.
 //   * P^T stays bf16 (as in the bf16 kernel) and O^T = V^T P^T runs on the
-//     bf16 MFMA: each V tile arrives as fp8 and is converted once, exactly
-//     (every e4m3 value is a bf16 value), into a bf16 LDS tile by all 256
-//     threads (v_cvt_scalef32_pk_bf16_fp8, 16 conversions per thread per
-//     64-key tile at d = 128), one tile ahead of its use.
+//     bf16 MFMA.  V stays fp8 in LDS: each operand is read with the 8-bit
+//     transposing load (ds_read_b64_tr_b8, 8 keys of one column per lane)
+//     and widened exactly in registers (every e4m3 value is a bf16 value;
+//     v_cvt_scalef32_pk_bf16_fp8, 4 per operand).  A first design converted
+//     each V tile once into a bf16 LDS tile; its LDS reads and writes cost
+//     about 14 % of the kernel, and widening per operand, inside the P V
+//     MFMA stream where the vector ALUs are otherwise idle, is 2.6 % faster
+//     than that design overall.
 // The caller folds the dequantisation factors of q and k into `scale`; the
 // factor of v multiplies the output (`v_scale`, applied in fp32 before the
 // final rounding).
@@ -30,9 +34,9 @@
 //   * K tiles: fp8 rows of d bytes, HBM -> LDS by DMA two tiles ahead; the
 //     16-byte chunks are XOR-swizzled by the row so that the operand reads
 //     (32 rows x one chunk) are conflict-free.
-//   * V tiles: fp8 staging ring filled by DMA two tiles ahead, converted to
-//     the bf16 ring one tile ahead; P V reads it transposed
-//     (ds_read_b64_tr_b16) exactly as the bf16 kernel does.
+//   * V tiles: fp8 rows, HBM -> LDS by DMA one tile ahead, their 32-byte
+//     bands XOR-swizzled by the row so that the transposing reads (16 rows x
+//     one band) are conflict-free.
 #include "kernels.h"
 
 #include <math.h>
@@ -47,9 +51,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr int BM = 128;
 constexpr int BN = 64;
@@ -67,10 +71,7 @@ struct Cfg {
     static constexpr int RPW8 = 64 / CH8;         // fp8 rows one wave-wide DMA covers
     static constexpr int ROUNDS8 = BN / (4 * RPW8);
     static constexpr int TILE8 = BN * D;          // bytes of an fp8 tile
-    static constexpr int TILE16 = BN * D;         // elements of a bf16 tile
-    static constexpr int EPT = BN * D / NTHR;     // V elements each thread converts
     static_assert(ROUNDS8 * 4 * RPW8 == BN, "tile split");
-    static_assert(EPT % 16 == 0, "whole 16-byte fp8 chunks per thread");
 };
 
 // Chunk swizzle of an fp8 K row (d bytes): 16 consecutive rows reading one
@@ -79,10 +80,13 @@ struct Cfg {
 template <int D> __device__ __forceinline__ int swz8(int row);
 template <> __device__ __forceinline__ int swz8<128>(int row) { return (row >> 1) & 7; }
 template <> __device__ __forceinline__ int swz8<64>(int row) { return (row >> 2) & 3; }
-// Chunk swizzle of the bf16 V tile (as the bf16 kernel's V tile).
-template <int D> __device__ __forceinline__ int swz_v(int row);
-template <> __device__ __forceinline__ int swz_v<128>(int row) { return (row & 3) << 2; }
-template <> __device__ __forceinline__ int swz_v<64>(int row) { return (row & 2) << 1; }
+// Chunk swizzle of the fp8 V tile: XOR on bits 1-2 of the 16-byte chunk index
+// (the 32-byte band), so that a transposing read of 16 consecutive rows x one
+// 32-byte band touches every bank once per 256 bytes (rows of 128 B: bits 1-2
+// of the row; rows of 64 B: bit 2).
+template <int D> __device__ __forceinline__ int swzw(int row);
+template <> __device__ __forceinline__ int swzw<128>(int row) { return ((row >> 1) & 3) << 1; }
+template <> __device__ __forceinline__ int swzw<64>(int row) { return ((row >> 2) & 1) << 1; }
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
@@ -104,10 +108,8 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_fp8_kernel(
     using C = Cfg<D>;
     __shared__ __attribute__((aligned(1024))) uint8_t sK0[C::TILE8];
     __shared__ __attribute__((aligned(1024))) uint8_t sK1[C::TILE8];
-    __shared__ __attribute__((aligned(1024))) uint8_t sW0[C::TILE8];  // fp8 V staging
+    __shared__ __attribute__((aligned(1024))) uint8_t sW0[C::TILE8];  // fp8 V tiles
     __shared__ __attribute__((aligned(1024))) uint8_t sW1[C::TILE8];
-    __shared__ __attribute__((aligned(1024))) __bf16 sV0[C::TILE16];  // bf16 V
-    __shared__ __attribute__((aligned(1024))) __bf16 sV1[C::TILE16];
 
     // ---- work item (same order and XCD remap as the bf16 kernel) ----------
     const int L = blockIdx.x;
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_fp8_kernel(
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const int ld_row = wave * C::RPW8 + lane / C::CH8, ld_slot = lane % C::CH8;
     const int voff_k = ld_row * D + ((ld_slot ^ swz8<D>(ld_row)) * 16);
-    const int voff_w = ld_row * D + ld_slot * 16;  // staging: plain row-major
+    const int voff_w = ld_row * D + ((ld_slot ^ swzw<D>(ld_row)) * 16);
     // BN fp8 rows base[row0 ..] into an LDS tile; rows past Nk read as 0
     // (the descriptor ends at the last row)
     // (the round stride is a named constant: this host compiler drops the
@@ -186,29 +188,6 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_fp8_kernel(
         }
     };
 
-    // ---- V conversion (fp8 staging -> swizzled bf16 tile) ---------------------
-    // thread tid converts row tid / (NTHR / BN), elements cv_e0 .. + EPT - 1
-    constexpr int TPR = NTHR / BN;  // threads per row
-    const int cv_row = tid / TPR, cv_e0 = (tid % TPR) * C::EPT;
-    auto convert = [&](const uint8_t *src, __bf16 *dst) {
-#pragma unroll
-        for (int c8 = 0; c8 < C::EPT / 16; ++c8) {
-            const u32x4 x = *reinterpret_cast<const u32x4 *>(src + cv_row * D + cv_e0 + 16 * c8);
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                u32x4 y;
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const uint32_t word = x[2 * half + i];
-                    y[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false));
-                    y[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true));
-                }
-                const int chunk = (cv_e0 + 16 * c8 + 8 * half) >> 3;  // bf16 chunk of 8 elements
-                *reinterpret_cast<u32x4 *>(dst + cv_row * D + ((chunk ^ swz_v<D>(cv_row)) * 8)) = y;
-            }
-        }
-    };
-
     // ---- running state -----------------------------------------------------
     f32x16 acc[C::CB];
 #pragma unroll
@@ -216,9 +195,6 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_fp8_kernel(
     float m_ref = -INFINITY;
     float l_run = 0.f;
 
-    const int tr_grp = lane >> 4, tr_j = lane & 15;
-    const int tr_key = 4 * (tr_grp >> 1) + (tr_j >> 2);
-    const int tr_col = 16 * (tr_grp & 1) + 4 * (tr_j & 3);
     // K operand: row n (+32 for the second key half, same swizzle), bytes
     // 64 s + 32 g .. + 31 = chunks 4 s + 2 g and 4 s + 2 g + 1
     int k_off[C::KS8][2];
@@ -226,11 +202,19 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_fp8_kernel(
     for (int s = 0; s < C::KS8; ++s)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) k_off[s][hf] = n * D + (((4 * s + 2 * g + hf) ^ swz8<D>(n)) * 16);
+    // V^T operand by ds_read_b64_tr_b8: in each 16-lane group G, output lane
+    // 16 G + 8 h + c receives byte c of the 8-byte reads of lanes 16 G + h,
+    // + 2, ..., + 14.  Lane a therefore reads the row holding the key that
+    // k-slot e = (a % 16) / 2 of output lanes 16 G + 8 h + .. needs (the key
+    // order of P^T: 4 g + {0..3, 8..11}, g = G / 2) at columns
+    // 32 cb + 16 (G % 2) + 8 h .. + 7.
     int v_off[C::CB];
+    {
+        const int G = lane >> 4, i = lane & 15, e = i >> 1, hb = i & 1;
+        const int rl = 4 * (G >> 1) + (e < 4 ? e : e + 4);  // key within the 16-key step
 #pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb) {
-        const int col = cb * 32 + tr_col;
-        v_off[cb] = tr_key * D + (((col >> 3) ^ swz_v<D>(tr_key)) * 8) + (col & 7);
+        for (int cb = 0; cb < C::CB; ++cb)
+            v_off[cb] = rl * D + (((2 * cb + (G & 1)) ^ swzw<D>(rl)) * 16) + 8 * hb;
     }
 
     auto kfrag = [&](const uint8_t *sk, int kt, int s) {
@@ -238,14 +222,16 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_fp8_kernel(
         const u32x4 hi = *reinterpret_cast<const u32x4 *>(sk + kt * 32 * D + k_off[s][1]);
         return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    auto vfrag = [&](const __bf16 *sv, int cb, int kt, int hh) {
-        i16x4 part[2];
+    // 8 fp8 values of one V column, widened exactly to bf16 in registers
+    auto vfrag = [&](const uint8_t *sw, int cb, int kt, int hh) {
+        const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(sw + (kt * 32 + 16 * hh) * D + v_off[cb]));
+        u32x4 y;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const __bf16 *p = sv + (kt * 32 + 16 * hh + 8 * half) * D + v_off[cb];
-            part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+        for (int wd = 0; wd < 2; ++wd) {
+            y[2 * wd] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)x[wd], 1.0f, false));
+            y[2 * wd + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)x[wd], 1.0f, true));
         }
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        return __builtin_bit_cast(bf16x8, y);
     };
     auto qk = [&](const uint8_t *sk, f32x16 (&st)[2]) {
         st[0] = f32x16{};
@@ -256,24 +242,20 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_fp8_kernel(
             for (int kt = 0; kt < 2; ++kt) st[kt] = mfma8(kfrag(sk, kt, s), qf[s], st[kt]);
     };
 
-    // Rings: K[j] in sK[j & 1], fp8 V[j] in sW[j & 1] (both DMA'd two tiles
-    // ahead), bf16 V[j] in sV[j & 1] (converted one tile ahead).  Iteration j
-    // starts K[j+2], W[j+2], converts W[j+1] -> V[j+1], computes the scores of
-    // tile j+1 with the softmax of tile j, then P V of tile j.
+    // Rings: K[j] in sK[j & 1] (DMA'd two tiles ahead), fp8 V[j] in sW[j & 1]
+    // (one tile ahead).  Iteration j starts K[j+2] and V[j+1], computes the
+    // scores of tile j+1 with the softmax of tile j, then P V of tile j.
     auto kbuf = [&](int j) { return (j & 1) ? sK1 : sK0; };
     auto wbuf = [&](int j) { return (j & 1) ? sW1 : sW0; };
-    auto vbuf = [&](int j) { return (j & 1) ? sV1 : sV0; };
-    auto dma = [&](int j) {
-        dma_rows8(Kh, j * BN, kbuf(j), voff_k);
-        dma_rows8(Vh, j * BN, wbuf(j), voff_w);
-    };
+    auto dma_k = [&](int j) { dma_rows8(Kh, j * BN, kbuf(j), voff_k); };
+    auto dma_w = [&](int j) { dma_rows8(Vh, j * BN, wbuf(j), voff_w); };
 
     auto iteration = [&](const int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
         const int j0 = j * BN;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K[j+1], W[j+1] have landed
-        __syncthreads();                                   // ... for every wave; tile j-1 is free
-        if (j + 2 < ntiles) dma(j + 2);
-        if (j + 1 < ntiles) convert(wbuf(j + 1), vbuf(j + 1));
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K[j+1], V[j] have landed
+        __syncthreads();                                   // ... for every wave; K[j], V[j-1] are free
+        if (j + 2 < ntiles) dma_k(j + 2);
+        if (j + 1 < ntiles) dma_w(j + 1);
         if (CAUSAL && j0 > wave_first_row + 31 + off) return;
 
         const bool need_mask = (j0 + BN > Nk) || (CAUSAL && j0 + BN - 1 > wave_first_row + off);
@@ -347,8 +329,8 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_fp8_kernel(
         }
         l_run += psum;
 
-        // O^T += V^T P^T for tile j (bf16 V tile)
-        const __bf16 *svc = vbuf(j);
+        // O^T += V^T P^T for tile j (fp8 V tile, widened per operand)
+        const uint8_t *svc = wbuf(j);
         constexpr int NPV = 4 * C::CB;
         constexpr int VAHEAD = 4;
         bf16x8 vq[NPV];
@@ -370,11 +352,11 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_fp8_kernel(
 
     f32x16 stA[2], stB[2];
     if (ntiles > 0) {
-        dma(0);
-        if (ntiles > 1) dma(1);
+        dma_k(0);
+        dma_w(0);
+        if (ntiles > 1) dma_k(1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        convert(wbuf(0), vbuf(0));
         qk(sK0, stA);
     }
     for (int j = 0; j < ntiles; j += 2) {
