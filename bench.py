@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-paged] [--no-rect]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-paged] [--no-graph] [--no-rect]
                     [--no-bwd] [--no-fp8] [--no-configs]
 
 One step is one pass of the whole path over synthetic inputs already resident
@@ -19,9 +19,10 @@ cache rows plus q, o, lse) in `decode`, and for each kernel its roofline
 fraction from its average duration measured with HIP events on the stream the
 kernels run on.  `cpu_baseline` times the fp64 oracle on a bounded sample of the
 prefill rows on the host cores, and (`per_config`) on each smaller prefill
-workload in full, next to that workload's GPU time.  `decode_paged` times the decode workload
-against a paged cache (block table over a shuffled pool) on its own, after the
-timed steps; `chunked_prefill` (a 2048-token chunk over 8192 cached tokens,
+workload in full, next to that workload's GPU time.  After the timed steps,
+`decode_graph` times the decode workload on its own, eager and replayed from a
+HIP graph, and `decode_paged` times it against a paged cache (block table over
+a shuffled pool); `chunked_prefill` (a 2048-token chunk over 8192 cached tokens,
 causal bottom-right) and `cross_attention` (2048 queries over 4096 keys,
 non-causal) time attn_fwd on the two rectangular workloads the same way;
 `backward` times attn_bwd (all three kernels) on the prefill workload with the
@@ -62,6 +63,7 @@ def parse():
     ap.add_argument("--only", choices=["prefill", "decode", "bwd", "fp8"], default=None,
                     help="run one kernel only (for profiling runs)")
     ap.add_argument("--no-paged", action="store_true", help="skip the paged-cache decode measurement")
+    ap.add_argument("--no-graph", action="store_true", help="skip the decode-alone and graph-replay measurement")
     ap.add_argument("--paged-block-size", type=int, default=64)
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 prefill measurement")
@@ -113,6 +115,49 @@ def paged_decode_line(E, A, I, dev, block_size, reps=4, steps=20, warmup=50):
             PEAK_HBM_GBS, 4), "avg_launch_ms": round(ms, 5), "block_size": block_size,
             "sum_seq_len": int(sl.sum()), "bytes_per_launch": by,
             "note": "same shape and lengths as the decode workload, rows in a shuffled pool of blocks"}
+
+
+def decode_graph_line(E, A, I, dev, qd, sl, caches, od, lsed, ws, steps=40, warmup=20, replays=20):
+    """The decode step on its own: eager back-to-back calls, and the same
+    calls replayed from a HIP graph that holds one call per cache replica
+    (the form a serving loop runs them in)."""
+    import torch
+
+    wd = I.WORKLOADS["C5"]
+
+    def call(i):
+        kc, vc = caches[i % len(caches)]
+        E.attn_decode(qd, kc, vc, sl, scale=wd.scale, o=od, lse=lsed, workspace=ws)
+
+    eager = timed_ms(call, steps, warmup)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up off the default stream before capture
+        for i in range(len(caches)):
+            call(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(len(caches)):
+            call(i)
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(replays):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    graph = t0.elapsed_time(t1) / (replays * len(caches))
+    by = A.decode_bytes(sl.cpu().tolist(), wd.Hq, wd.Hkv, wd.d, wd.dtype)
+    return {"value": round(by / (graph * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "frac_hbm": round(by / (graph * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "graph_call_ms": round(graph, 5),
+            "eager_alone_ms": round(eager, 5),
+            "eager_alone_gbs": round(by / (eager * 1e-3) / 1e9, 1),
+            "note": "the decode workload on its own (not after a prefill): eager back-to-back calls, and the same "
+                    "calls replayed from a HIP graph of one call per cache replica"}
 
 
 def timed_ms(call, steps, warmup):
@@ -420,6 +465,8 @@ def main():
             "frac": round(d_gbs / PEAK_HBM_GBS, 4), "traffic": tr,
             "kernel": "decode_chunk_kernel<128,4,3> + decode_merge_kernel<128>", "avg_launch_ms": round(d_ms, 5),
         }
+    if run_d and not args.no_graph:
+        out["decode_graph"] = decode_graph_line(E, A, I, dev, qd, sl, caches, od, lsed, ws)
     if run_d and not args.no_paged:
         out["decode_paged"] = paged_decode_line(E, A, I, dev, args.paged_block_size)
     if run_b:
