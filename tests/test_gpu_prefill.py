@@ -63,6 +63,7 @@ RAGGED = [
     # causal chunks with enough 256-row work items: the 8-wave kernel
     ("bf16", 64, 2, 128, 16, 300, 1000, True),
     ("bf16", 128, 2, 128, 16, 300, 700, True),
+    ("bf16", 64, 2, 128, 8, 300, 260, False),   # non-causal, Nk < Nq, 8 waves
     ("f32", 64, 2, 2, 1, 100, 100, True),
     ("f32", 128, 1, 4, 2, 70, 130, True),
     ("f32", 128, 1, 2, 1, 33, 17, False),
