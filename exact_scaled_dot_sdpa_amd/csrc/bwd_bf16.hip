@@ -323,15 +323,28 @@ __global__ __launch_bounds__(NTHR, 2) void bwd_dq_kernel(
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             f32x16 st = f32x16{}, dp = f32x16{};
+            // the two chains alternate, their operands read AH k-steps ahead
+            // (so every MFMA finds its operands in registers: with the
+            // chains one after the other the compiler kept a single K
+            // operand in flight and each score MFMA waited for its read)
+            constexpr int AH = 2;
+            bf16x8 kq[C::KS], vq[C::KS];
+            auto rk = [&](int s_) { return *reinterpret_cast<const bf16x8 *>(sk + kt * 32 * D + k_off[s_]); };
+            auto rv = [&](int s_) { return *reinterpret_cast<const bf16x8 *>(sv + kt * 32 * D + v_off[s_]); };
 #pragma unroll
-            for (int s = 0; s < C::KS; ++s) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(sk + kt * 32 * D + k_off[s]);
-                st = mfma(ka, qf[s], st);
+            for (int s = 0; s < AH; ++s) {
+                kq[s] = rk(s);
+                vq[s] = rv(s);
             }
 #pragma unroll
             for (int s = 0; s < C::KS; ++s) {
-                const bf16x8 va = *reinterpret_cast<const bf16x8 *>(sv + kt * 32 * D + v_off[s]);
-                dp = mfma(va, df[s], dp);
+                if (s + AH < C::KS) {
+                    kq[s + AH] = rk(s + AH);
+                    vq[s + AH] = rv(s + AH);
+                }
+                st = mfma(kq[s], qf[s], st);
+                dp = mfma(vq[s], df[s], dp);
+                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -339,11 +352,19 @@ __global__ __launch_bounds__(NTHR, 2) void bwd_dq_kernel(
                 if (need_mask && kt * 32 + 8 * (r >> 2) + (r & 3) > rel) p = 0.f;
                 st[r] = p * (dp[r] - dd);
             }
+            {
+                constexpr int NT = 2 * C::CB, TA = 3;  // K^T operands read TA MFMAs ahead
+                bf16x8 tq[NT];
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const bf16x8 bs = pack_b(st, hh);
+                for (int i = 0; i < TA; ++i) tq[i] = tr_frag<D>(sk, kt_off, i % C::CB, 2 * kt + i / C::CB);
+                const bf16x8 bs0 = pack_b(st, 0), bs1 = pack_b(st, 1);
 #pragma unroll
-                for (int cb = 0; cb < C::CB; ++cb) acc[cb] = mfma(tr_frag<D>(sk, kt_off, cb, 2 * kt + hh), bs, acc[cb]);
+                for (int i = 0; i < NT; ++i) {
+                    if (i + TA < NT) tq[i + TA] = tr_frag<D>(sk, kt_off, (i + TA) % C::CB, 2 * kt + (i + TA) / C::CB);
+                    const int cb = i % C::CB, hh = i / C::CB;
+                    acc[cb] = mfma(tq[i], hh ? bs1 : bs0, acc[cb]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
     };
@@ -477,15 +498,29 @@ __global__ __launch_bounds__(KNW * 64) void bwd_dkdv_kernel(
         const float *sl = lbuf(u) + qh * 32, *se = ebuf(u) + qh * 32;
 
         // S = Q K^T and dP = dO V^T for 32 rows x 32 keys
+        // the two chains alternate, their four operands read two k-steps
+        // ahead (one chain after the other, each MFMA waited for its own
+        // two reads)
         f32x16 sc = f32x16{}, dp = f32x16{};
+        {
+            constexpr int AH = 2;
+            bf16x8 qa[C::KS], ka[C::KS], da[C::KS], va[C::KS];
+            auto rd = [&](int s_) {
+                qa[s_] = *reinterpret_cast<const bf16x8 *>(sq + rq_base + (((2 * s_) ^ x_rt) * 8));
+                ka[s_] = *reinterpret_cast<const bf16x8 *>(sK + rv_base + (((2 * s_) ^ x_rows) * 8));
+                da[s_] = *reinterpret_cast<const bf16x8 *>(sd + rq_base + (((2 * s_) ^ x_rt) * 8));
+                va[s_] = *reinterpret_cast<const bf16x8 *>(sV + rv_base + (((2 * s_) ^ x_rows) * 8));
+            };
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s)
-            sc = mfma(*reinterpret_cast<const bf16x8 *>(sq + rq_base + (((2 * s) ^ x_rt) * 8)),
-                      *reinterpret_cast<const bf16x8 *>(sK + rv_base + (((2 * s) ^ x_rows) * 8)), sc);
+            for (int s = 0; s < AH; ++s) rd(s);
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s)
-            dp = mfma(*reinterpret_cast<const bf16x8 *>(sd + rq_base + (((2 * s) ^ x_rt) * 8)),
-                      *reinterpret_cast<const bf16x8 *>(sV + rv_base + (((2 * s) ^ x_rows) * 8)), dp);
+            for (int s = 0; s < C::KS; ++s) {
+                if (s + AH < C::KS) rd(s + AH);
+                sc = mfma(qa[s], ka[s], sc);
+                dp = mfma(da[s], va[s], dp);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
         // P and dS: lane (n, g) holds key kj and rows qb + 8 rr + 4 g + i
         const bool need_mask = (qb + 32 > Nq) || (wk0 + 32 > Nk) || (CAUSAL && wk0 + 31 > qb + off);
         u32x4 bp[2];
