@@ -487,6 +487,7 @@ def main():
         for name, rec in out["cpu_baseline"].get("per_config", {}).items():
             if name in out.get("other_configs", {}):
                 rec["gpu_us"] = out["other_configs"][name]["us"]
+                rec["gpu_speedup"] = round(rec["seconds"] / (rec["gpu_us"] * 1e-6), 1)
     print(json.dumps(out), flush=True)
 
 
