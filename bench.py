@@ -20,6 +20,7 @@ fraction from its average duration measured with HIP events on the stream the
 kernels run on.  `cpu_baseline` times the fp64 oracle on a bounded sample of the
 prefill rows on the host cores, and (`per_config`) on each smaller prefill
 workload in full, next to that workload's GPU time.  After the timed steps,
+`startup` gives the library load and each kernel's first (cold) call;
 `decode_graph` times the decode workload on its own, eager and replayed from a
 HIP graph, and `decode_paged` times it against a paged cache (block table over
 a shuffled pool); `chunked_prefill` (a 2048-token chunk over 8192 cached tokens,
@@ -353,6 +354,12 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
+    # one-time costs, reported apart from the timed steps: loading the library,
+    # and (below) the first call of each kernel, which also loads its code
+    t0 = time.perf_counter()
+    E.lib()
+    startup = {"lib_load_ms": round((time.perf_counter() - t0) * 1e3, 3)}
+
     wp = I.WORKLOADS["C4"]
     wd = I.WORKLOADS["C5"]
     run_p = args.only in (None, "prefill")
@@ -394,6 +401,14 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    for name, fn, on in (("first_prefill_ms", prefill, run_p), ("first_decode_ms", lambda: decode(0), run_d)):
+        if on:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            startup[name] = round((time.perf_counter() - t0) * 1e3, 3)
 
     for i in range(args.warmup):
         if run_p:
@@ -465,6 +480,8 @@ def main():
             "frac": round(d_gbs / PEAK_HBM_GBS, 4), "traffic": tr,
             "kernel": "decode_chunk_kernel<128,4,3> + decode_merge_kernel<128>", "avg_launch_ms": round(d_ms, 5),
         }
+    out["startup"] = dict(startup, note="library load and the first call of each kernel (code-object load "
+                          "included), against the warm per-call times above; compilation happens at build time")
     if run_d and not args.no_graph:
         out["decode_graph"] = decode_graph_line(E, A, I, dev, qd, sl, caches, od, lsed, ws)
     if run_d and not args.no_paged:
