@@ -40,7 +40,8 @@ def max_err(a, b):
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
     both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
-    d = np.where(both_inf, 0.0, np.abs(a - b))
+    with np.errstate(invalid="ignore"):  # inf - inf of equal infinities is masked out here
+        d = np.where(both_inf, 0.0, np.abs(a - b))
     if np.isnan(d).any():
         return float("nan")
     return float(d.max()) if d.size else 0.0
@@ -52,6 +53,32 @@ def assert_close(name, got, ref, tol):
     assert e == e, "%s: NaN in the result" % name
     assert e <= tol, "%s: max-abs err %.3e > %.1e" % (name, e, tol)
     return e
+
+
+def grad_floors(orc, q, k, v, do, scale, causal):
+    """Absolute error floors for the gradient checks, which are otherwise
+    relative to each reference tensor's largest entry.  ds = p (dp - D)
+    cancels: where a row sees a single key it is exactly 0 by definition (o is
+    that key's v), while the kernels form dp on the MFMA and D = do . o in
+    another summation order, so ds is fp32 rounding noise of at most
+    eps = d 2^-22 max|do| max|v| per entry (16 d unit roundoffs of the
+    products' scale), and a reference that is 0 everywhere (every row sees one
+    key) leaves the relative bound no room for it.  That noise reaches
+      dq_i = scale sum_j ds_ij k_j  weighted by p_ij, which sums to 1 over j:
+             floor |scale| max|k| eps;
+      dk_j = scale sum_i ds_ij q_i  weighted by the column sums of P (over the
+             query rows and the heads that share key j): floor |scale| max|q|
+             eps max_j sum_i p_ij, the column sums read off the oracle's dv
+             for do = 1;
+      dv   has no such cancellation: floor 0."""
+    q64, k64, v64, do64 = (I.to_f64(t) for t in (q, k, v, do))
+    if q64.size == 0 or k64.size == 0:
+        return {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    eps = q64.shape[3] * 2.0 ** -22 * np.abs(do64).max() * np.abs(v64).max()
+    col = orc.attn_bwd(q64, k64, v64, np.ones_like(do64), scale, causal)[2]
+    return {"dq": abs(scale) * np.abs(k64).max() * eps,
+            "dk": abs(scale) * np.abs(q64).max() * eps * float(np.abs(col).max()),
+            "dv": 0.0}
 
 
 def sample_rows(B, H, N, n_random, seed, extra_i=()):

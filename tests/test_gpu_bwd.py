@@ -10,7 +10,10 @@ accumulation in between.  Compared with the largest magnitude of the
 gradient tensor this stays below 3 * 2^-9 = 5.9e-3 per contribution; sums of
 such errors over rows grow more slowly than the sums themselves.  The test
 bounds max |g - ref| by 2e-2 * max |ref| per tensor (about five bf16 ulps of
-the largest entry) and the RMS error by 6e-3 * RMS(ref).
+the largest entry) and the RMS error by 6e-3 * RMS(ref), each plus an absolute
+floor for dq and dk at the fp32 rounding scale of the cancellation in
+ds = p (dp - D) (gpu_util.grad_floors): with a single key in every row, dq and
+dk are exactly zero and the kernels return rounding noise.
 """
 import numpy as np
 import pytest
@@ -18,7 +21,7 @@ import torch
 
 import exact_scaled_dot_sdpa_amd as E
 from exact_scaled_dot_sdpa_amd import inputs as I
-from gpu_util import dev, say
+from gpu_util import dev, grad_floors, say
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +38,7 @@ def gpu_fwd_bwd(q, k, v, do, scale, causal):
     return I.to_f64(dq), I.to_f64(dk), I.to_f64(dv)
 
 
-def check_grad(name, got, ref):
+def check_grad(name, got, ref, floor=0.0):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert np.isfinite(got).all(), "%s: non-finite gradient" % name
@@ -47,8 +50,10 @@ def check_grad(name, got, ref):
     e_rms = float(np.sqrt(np.mean((got - ref) ** 2)))
     say("  %-34s max err %.3e = %.2e of max|ref| %.3e; rms err %.2e of rms" %
         (name, e_max, e_max / max(scale_max, 1e-300), scale_max, e_rms / max(scale_rms, 1e-300)))
-    assert e_max <= TOL_MAX * scale_max, "%s: max err %.3e > %.1e * %.3e" % (name, e_max, TOL_MAX, scale_max)
-    assert e_rms <= TOL_RMS * scale_rms, "%s: rms err %.3e > %.1e * %.3e" % (name, e_rms, TOL_RMS, scale_rms)
+    assert e_max <= TOL_MAX * scale_max + floor, "%s: max err %.3e > %.1e * %.3e + %.1e" % (
+        name, e_max, TOL_MAX, scale_max, floor)
+    assert e_rms <= TOL_RMS * scale_rms + floor, "%s: rms err %.3e > %.1e * %.3e + %.1e" % (
+        name, e_rms, TOL_RMS, scale_rms, floor)
 
 
 CASES = [
@@ -76,9 +81,10 @@ def test_bwd_parity(orc, case):
     scale = 1.0 / np.sqrt(d)
     dq, dk, dv = gpu_fwd_bwd(q, k, v, do, scale, causal)
     rq, rk, rv = orc.attn_bwd(I.to_f64(q), I.to_f64(k), I.to_f64(v), I.to_f64(do), scale, causal)
-    check_grad("dq", dq, rq)
-    check_grad("dk", dk, rk)
-    check_grad("dv", dv, rv)
+    fl = grad_floors(orc, q, k, v, do, scale, causal)
+    check_grad("dq", dq, rq, fl["dq"])
+    check_grad("dk", dk, rk, fl["dk"])
+    check_grad("dv", dv, rv, fl["dv"])
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.3, 0.5])
@@ -93,8 +99,9 @@ def test_bwd_scales(orc, scale):
         if scale == 0.0:
             assert np.all(dq == 0) and np.all(dk == 0), "scale 0: dq and dk must vanish"
         else:
-            check_grad("dq", dq, rq)
-            check_grad("dk", dk, rk)
+            fl = grad_floors(orc, q, k, v, do, scale, causal)
+            check_grad("dq", dq, rq, fl["dq"])
+            check_grad("dk", dk, rk, fl["dk"])
         check_grad("dv", dv, rv)
 
 
