@@ -468,7 +468,7 @@ def main():
         out["roofline"] = {
             "bound": "mfma", "achieved": round(p_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4), "traffic": tr,
-            "kernel": "prefill_bf16_kernel<128,true,4>", "avg_launch_ms": round(p_ms, 5),
+            "kernel": "prefill_bf16_kernel<128,true,8,8>", "avg_launch_ms": round(p_ms, 5),
         }
     if run_d:
         tr = stored_traffic("decode")

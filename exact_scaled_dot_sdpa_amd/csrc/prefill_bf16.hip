@@ -7,15 +7,23 @@
 // un-normalised accumulator recurrence).
 //
 // gfx950 mapping
-//   * A workgroup owns BM = 32 NW query rows of one (batch, query head); each
-//     of its NW waves owns 32 rows.  K/V are streamed in tiles of BN = 64 keys.
-//     NW = 4 (two workgroups per CU) in general; NW = 8 (one workgroup per CU,
-//     still two waves per SIMD) when every row sees a similar number of keys
-//     (non-causal, or a causal chunk at least as far from the start as it is
-//     long) and there are at least two such workgroups per CU: each K/V tile
-//     staged in LDS then serves twice as many rows, which was about 3.5 %
-//     faster there, while on the square causal layer the coarser balancing of
-//     the triangular work cancels the gain.
+//   * A workgroup has NW waves of 32 query rows each, all of one (batch, K/V
+//     head), and streams that head's K/V in tiles of BN = 64 keys.  The waves
+//     cover HP query heads of the K/V head's group at 32 NW / HP query
+//     positions.  Three forms:
+//       - NW = 4, HP = 1: 128 rows of one head, two workgroups per CU (the
+//         general case);
+//       - NW = 8, HP = 1: 256 rows of one head, one workgroup per CU, still two
+//         waves per SIMD, when every row sees a similar number of keys
+//         (non-causal, or a causal chunk at least as far from the start as it
+//         is long): each K/V tile staged in LDS serves twice as many rows;
+//       - NW = 8, HP = 8 (or 4): 32 (or 64) query positions of 8 (or 4) heads,
+//         for causal GQA layers whose rows sit at very different depths.  Each
+//         tile again serves 256 rows, and since the waves share their query
+//         positions they share the causal key range, so the triangular work
+//         stays as finely balanced as with 32-row tiles.
+//     The wide forms are used when the grid still holds two workgroups per
+//     CU.  Each row's arithmetic is the same in every form.
 //   * K and V tiles go from HBM straight into LDS with global_load_lds_dwordx4
 //     (no staging registers, no VALU work), double-buffered so the next tile
 //     lands while the current one is computed; one barrier per tile.  Both
@@ -44,9 +52,10 @@
 //     masked code path.  Bottom-right alignment: row i sees j <= i + Nk - Nq.
 //   * GQA: query head h reads K/V head h / (Hq / Hkv).  Work items are
 //     ordered (batch, KV head) outermost, then query tile (heaviest causal
-//     tile first), then the G query heads of the group, and spread over the
-//     8 XCDs in contiguous chunks, so the query heads sharing a K/V head run
-//     on one XCD at the same time and read that head's K/V through one L2.
+//     tile first), then the G / HP head blocks of the group, and spread over
+//     the 8 XCDs in contiguous chunks, so the query heads sharing a K/V head
+//     run on one XCD at the same time and read that head's K/V through one
+//     L2.
 #include "kernels.h"
 
 #include <math.h>
@@ -112,14 +121,14 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-template <int D, bool CAUSAL, int NW>
+template <int D, bool CAUSAL, int NW, int HP>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
     __bf16 *__restrict__ O, float *__restrict__ LSE, int Hq, int Hkv, int Nq, int Nk,
     float sl2, int n_qtiles, int total)
 {
     using C = Cfg<D, NW>;
-    constexpr int BM = C::BM;
+    constexpr int BMP = 32 * (NW / HP);  // query positions per workgroup
     // double-buffered K and V tiles, row-major, chunk-swizzled
     __shared__ __attribute__((aligned(1024))) __bf16 sK0[C::TILE];
     __shared__ __attribute__((aligned(1024))) __bf16 sK1[C::TILE];
@@ -132,18 +141,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(
     const int per = total >> 3, rem = total & 7;
     const int w = xcd * per + (xcd < rem ? xcd : rem) + local;
     const int G = Hq / Hkv;
-    const int gq = w % G;
-    int t = w / G;
+    const int nhb = G / HP;
+    const int gqb = w % nhb;
+    int t = w / nhb;
     const int tq_ord = t % n_qtiles;
     t /= n_qtiles;
     const int hk = t % Hkv;
     const int b = t / Hkv;
-    const int h = hk * G + gq;
     const int tq = CAUSAL ? (n_qtiles - 1 - tq_ord) : tq_ord;
-    const int q0 = tq * BM;
+    const int q0 = tq * BMP;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int h = hk * G + gqb * HP + wave_u % HP;  // this wave's query head
+    const int prow = q0 + (wave_u / HP) * 32;       // this wave's first query row
     const int n = lane & 31, g = lane >> 5;
     const int off = Nk - Nq;  // bottom-right causal offset
 
@@ -152,7 +164,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(
     const __bf16 *Vh = V + ((size_t)(b * Hkv + hk) * Nk) * D;
 
     // ---- Q^T operands, resident for the whole kernel ---------------------
-    const int qi = q0 + wave * 32 + n;  // this lane's query row
+    const int qi = prow + n;  // this lane's query row
     bf16x8 qf[C::KS];
     if (qi < Nq) {
         const bf16x8 *src = reinterpret_cast<const bf16x8 *>(Qh + (size_t)qi * D + 8 * g);
@@ -180,7 +192,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(
     // ---- key range --------------------------------------------------------
     int kv_end = Nk;
     if (CAUSAL) {
-        const int last_row = (q0 + BM < Nq ? q0 + BM : Nq);  // exclusive
+        const int last_row = (q0 + BMP < Nq ? q0 + BMP : Nq);  // exclusive
         const int e = last_row + off;                        // keys < e are visible to some row
         kv_end = e < Nk ? e : Nk;
     }
@@ -188,7 +200,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(
 
     // per-lane limit of visible keys (inclusive)
     const int lim = CAUSAL ? ((qi + off) < (Nk - 1) ? (qi + off) : (Nk - 1)) : (Nk - 1);
-    const int wave_first_row = q0 + wave * 32;
+    const int wave_first_row = prow;
 
     // ---- HBM -> LDS tile loads -------------------------------------------
     // One wave-wide buffer_load_dwordx4 ... lds fills RPW consecutive rows
@@ -443,15 +455,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(
     }
 }
 
-template <int D, bool CAUSAL, int NW>
+template <int D, bool CAUSAL, int NW, int HP>
 hipError_t launch_nw(const FwdArgs &a, hipStream_t stream) {
     using C = Cfg<D, NW>;
+    constexpr int BMP = 32 * (NW / HP);
     const float sl2 = a.scale * LOG2E;
-    const int n_qtiles = (a.Nq + C::BM - 1) / C::BM;
-    const long long total = (long long)a.B * a.Hq * n_qtiles;
+    const int n_qtiles = (a.Nq + BMP - 1) / BMP;
+    const long long total = (long long)a.B * (a.Hq / HP) * n_qtiles;
     if (total <= 0) return hipSuccess;
     if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, NW>), dim3((unsigned)total), dim3(C::NTHR), 0, stream,
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, NW, HP>), dim3((unsigned)total), dim3(C::NTHR), 0, stream,
                        (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v, (__bf16 *)a.o,
                        a.lse, a.Hq, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles, (int)total);
     return hipGetLastError();
@@ -477,17 +490,27 @@ hipError_t cu_count(int *out) {
 
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs &a, hipStream_t stream) {
-    // 8-wave workgroups when the rows see similar numbers of keys and the
-    // grid still holds at least two of them per CU
+    int cus = 0;
+    const hipError_t e = cu_count(&cus);
+    if (e != hipSuccess) return e;
+    const long long two_per_cu = 2LL * cus;
+    // 8-wave workgroups of 256 rows of one head when the rows see similar
+    // numbers of keys and the grid still holds at least two of them per CU
     const bool even_rows = !CAUSAL || (long long)a.Nk - a.Nq >= a.Nq;
     if (even_rows) {
-        int cus = 0;
-        const hipError_t e = cu_count(&cus);
-        if (e != hipSuccess) return e;
-        const long long wide = (long long)a.B * a.Hq * ((a.Nq + Cfg<D, 8>::BM - 1) / Cfg<D, 8>::BM);
-        if (wide >= 2LL * cus) return launch_nw<D, CAUSAL, 8>(a, stream);
+        const long long wide = (long long)a.B * a.Hq * ((a.Nq + 255) / 256);
+        if (wide >= two_per_cu) return launch_nw<D, CAUSAL, 8, 1>(a, stream);
     }
-    return launch_nw<D, CAUSAL, 4>(a, stream);
+    if constexpr (CAUSAL) {
+        // rows at different depths: 8-wave workgroups over the same 32 (64)
+        // query positions of 8 (4) heads that share a K/V head
+        const int G = a.Hq / a.Hkv;
+        if (!even_rows && G % 8 == 0 && (long long)a.B * (a.Hq / 8) * ((a.Nq + 31) / 32) >= two_per_cu)
+            return launch_nw<D, CAUSAL, 8, 8>(a, stream);
+        if (!even_rows && G % 4 == 0 && (long long)a.B * (a.Hq / 4) * ((a.Nq + 63) / 64) >= two_per_cu)
+            return launch_nw<D, CAUSAL, 8, 4>(a, stream);
+    }
+    return launch_nw<D, CAUSAL, 4, 1>(a, stream);
 }
 
 }  // namespace
