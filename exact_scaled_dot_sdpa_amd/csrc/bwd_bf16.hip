@@ -18,15 +18,19 @@
 // Three kernels, no atomics, deterministic:
 //   * bwd_pre_kernel: D_i and lse_i * log2(e) for every row (HBM-bound,
 //     reads o and do once).
-//   * bwd_dq_kernel: a workgroup owns 128 query rows (32 per wave) of one
-//     query head; Q^T and dO^T stay in registers as MFMA B operands while
+//   * bwd_dq_kernel: each wave owns 32 query rows, and a workgroup's waves
+//     all read one K/V head: 4 waves over 128 rows of one query head, or, on
+//     causal layers whose rows sit at very different depths, 8 waves over the
+//     same 32 (64) query positions of 8 (4) heads of the group, as in the
+//     forward.  Q^T and dO^T stay in registers as MFMA B operands while
 //     K/V tiles of 64 keys stream through LDS (DMA, double-buffered).  Per
 //     32-key half of a tile: S^T = K Q^T and dP^T = V dO^T
 //     (v_mfma_f32_32x32x16_bf16), P^T and dS^T on the vector ALUs, then
 //     dQ^T += K^T dS^T, where dS^T (bf16) is used straight from the
 //     accumulator layout as the B operand and K^T is read from the row-major
-//     K tile with ds_read_b64_tr_b16.  Two workgroups per CU (two waves per
-//     SIMD), so one wave's exp / VALU work hides behind another's MFMAs.
+//     K tile with ds_read_b64_tr_b16.  Two waves per SIMD (two 4-wave
+//     workgroups or one 8-wave workgroup per CU), so one wave's exp / VALU
+//     work hides behind another's MFMAs.
 //   * bwd_dkdv_kernel: a workgroup of 8 waves owns 128 keys of one K/V head;
 //     its K and V rows stay resident in LDS while Q / dO tiles of 64 rows of every
 //     query head of the GQA group stream through LDS, so dK and dV are summed
@@ -61,7 +65,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int NTHR = 256;
-constexpr int BM = 128;   // dq kernel: query rows per workgroup
 constexpr int BN = 64;    // dq kernel: keys per tile
 constexpr int BKN = 128;  // dkdv kernel: keys per workgroup
 constexpr int BQ = 64;    // dkdv kernel: query rows per tile
@@ -216,8 +219,8 @@ __global__ __launch_bounds__(NTHR) void bwd_pre_kernel(const __bf16 *__restrict_
 }
 
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(NTHR, 2) void bwd_dq_kernel(
+template <int D, bool CAUSAL, int NW, int HP>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
     const __bf16 *__restrict__ dO, const float *__restrict__ L2, const float *__restrict__ Dv,
     __bf16 *__restrict__ dQ, int Hq, int Hkv, int Nq, int Nk, float sl2, float scale, int n_qtiles, int total)
@@ -229,20 +232,24 @@ __global__ __launch_bounds__(NTHR, 2) void bwd_dq_kernel(
     __shared__ __attribute__((aligned(1024))) __bf16 sV1[BN * D];
 
     // work item: (batch, KV head) outermost, then query tile (heaviest causal
-    // tile first), then the query heads of the group
+    // tile first), then the blocks of HP query heads of the group; the NW
+    // waves cover HP heads at BMP query positions
+    constexpr int BMP = 32 * (NW / HP);
     const int w = xcd_remap(blockIdx.x, total);
     const int G = Hq / Hkv;
-    const int gq = w % G;
-    int t = w / G;
+    const int nhb = G / HP;
+    const int gqb = w % nhb;
+    int t = w / nhb;
     const int tq_ord = t % n_qtiles;
     t /= n_qtiles;
     const int hk = t % Hkv, b = t / Hkv;
-    const int h = hk * G + gq;
-    const int q0 = (CAUSAL ? (n_qtiles - 1 - tq_ord) : tq_ord) * BM;
+    const int q0 = (CAUSAL ? (n_qtiles - 1 - tq_ord) : tq_ord) * BMP;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 31, g = lane >> 5;
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int h = hk * G + gqb * HP + wave_s % HP;  // this wave's query head
+    const int prow = q0 + (wave_s / HP) * 32;       // this wave's first query row
     const int off = Nk - Nq;
 
     const size_t qrow0 = (size_t)(b * Hq + h) * Nq;
@@ -250,7 +257,7 @@ __global__ __launch_bounds__(NTHR, 2) void bwd_dq_kernel(
     const __bf16 *Vh = V + (size_t)(b * Hkv + hk) * Nk * D;
 
     // Q^T and dO^T operands of this lane's query row, resident
-    const int qi = q0 + wave * 32 + n;
+    const int qi = prow + n;
     bf16x8 qf[C::KS], df[C::KS];
     float lse2 = 0.f, dd = 0.f;
     if (qi < Nq) {
@@ -273,12 +280,12 @@ __global__ __launch_bounds__(NTHR, 2) void bwd_dq_kernel(
 
     int kv_end = Nk;
     if (CAUSAL) {
-        const int last_row = q0 + BM < Nq ? q0 + BM : Nq;
+        const int last_row = q0 + BMP < Nq ? q0 + BMP : Nq;
         kv_end = last_row + off < Nk ? last_row + off : Nk;
     }
     const int ntiles = (kv_end + BN - 1) / BN;
     const int lim = CAUSAL ? (qi + off < Nk - 1 ? qi + off : Nk - 1) : Nk - 1;  // last visible key
-    const int wave_first_row = q0 + wave * 32;
+    const int wave_first_row = prow;
 
     // DMA lane offsets: K is read row-wise and transposed, V row-wise only
     const int ld_row = wave * C::RPW + lane / C::CH, ld_slot = lane % C::CH;
@@ -299,8 +306,8 @@ __global__ __launch_bounds__(NTHR, 2) void bwd_dq_kernel(
     for (int cb = 0; cb < C::CB; ++cb) acc[cb] = f32x16{};
 
     auto load = [&](int j, __bf16 *k_dst, __bf16 *v_dst) {
-        dma_tile<D, BN, 4>(Kh, j * BN, Nk, k_dst, voff_k, wave_s);
-        dma_tile<D, BN, 4>(Vh, j * BN, Nk, v_dst, voff_v, wave_s);
+        dma_tile<D, BN, NW>(Kh, j * BN, Nk, k_dst, voff_k, wave_s);
+        dma_tile<D, BN, NW>(Vh, j * BN, Nk, v_dst, voff_v, wave_s);
     };
 
     if (ntiles > 0) load(0, sK0, sV0);
@@ -605,6 +612,39 @@ __global__ __launch_bounds__(KNW * 64) void bwd_dkdv_kernel(
     }
 }
 
+template <int D, bool CAUSAL, int NW, int HP>
+hipError_t launch_dq_form(const BwdArgs &a, float sl2, long long rows, hipStream_t stream) {
+    constexpr int BMP = 32 * (NW / HP);
+    const int n_qtiles = (a.Nq + BMP - 1) / BMP;
+    const long long total = (long long)a.B * (a.Hq / HP) * n_qtiles;
+    if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, NW, HP>), dim3((unsigned)total), dim3(64 * NW), 0, stream,
+                       (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
+                       (const __bf16 *)a.dout, (const float *)(a.ws_d + rows), (const float *)a.ws_d,
+                       (__bf16 *)a.dq, a.Hq, a.Hkv, a.Nq, a.Nk, sl2, a.scale, n_qtiles, (int)total);
+    return hipGetLastError();
+}
+
+// The dq kernel's workgroup forms follow the forward's: for causal layers
+// whose rows sit at very different depths, 8 waves over the same query
+// positions of 8 (or 4) heads that share a K/V head, so that each K/V tile
+// staged in LDS serves 256 rows; otherwise 4 waves over 128 rows of one head.
+template <int D, bool CAUSAL>
+hipError_t launch_dq(const BwdArgs &a, float sl2, long long rows, hipStream_t stream) {
+    if constexpr (CAUSAL) {
+        int cus = 0;
+        const hipError_t e = device_cu_count(&cus);
+        if (e != hipSuccess) return e;
+        const bool even_rows = (long long)a.Nk - a.Nq >= a.Nq;
+        const int G = a.Hq / a.Hkv;
+        if (!even_rows && G % 8 == 0 && (long long)a.B * (a.Hq / 8) * ((a.Nq + 31) / 32) >= 2LL * cus)
+            return launch_dq_form<D, CAUSAL, 8, 8>(a, sl2, rows, stream);
+        if (!even_rows && G % 4 == 0 && (long long)a.B * (a.Hq / 4) * ((a.Nq + 63) / 64) >= 2LL * cus)
+            return launch_dq_form<D, CAUSAL, 8, 4>(a, sl2, rows, stream);
+    }
+    return launch_dq_form<D, CAUSAL, 4, 1>(a, sl2, rows, stream);
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch(const BwdArgs &a, hipStream_t stream) {
     const float sl2 = a.scale * LOG2E;
@@ -615,14 +655,8 @@ hipError_t launch(const BwdArgs &a, hipStream_t stream) {
         if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)blocks), dim3(NTHR), 0, stream,
                            (const __bf16 *)a.o, (const __bf16 *)a.dout, a.lse, a.ws_d, a.ws_d + rows, rows);
-        const int n_qtiles = (a.Nq + BM - 1) / BM;
-        const long long total = (long long)a.B * a.Hq * n_qtiles;
-        if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)total), dim3(NTHR), 0, stream,
-                           (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v,
-                           (const __bf16 *)a.dout, (const float *)(a.ws_d + rows), (const float *)a.ws_d,
-                           (__bf16 *)a.dq, a.Hq, a.Hkv,
-                           a.Nq, a.Nk, sl2, a.scale, n_qtiles, (int)total);
+        const hipError_t e = launch_dq<D, CAUSAL>(a, sl2, rows, stream);
+        if (e != hipSuccess) return e;
     }
     const int n_ktiles = (a.Nk + BKN - 1) / BKN;
     const long long total_k = (long long)a.B * a.Hkv * n_ktiles;

@@ -60,4 +60,7 @@ hipError_t launch_prefill_fp8(const Fp8FwdArgs &a, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream);
 
+// Compute units of the current device (queried once per device, cached).
+hipError_t device_cu_count(int *out);
+
 }  // namespace attn

@@ -470,28 +470,10 @@ hipError_t launch_nw(const FwdArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Compute units of the current device, queried once per device.
-hipError_t cu_count(int *out) {
-    static std::atomic<int> cached[64];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    int cus = cached[dev].load(std::memory_order_relaxed);
-    if (cus == 0) {
-        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        cus = cus > 0 ? cus : 1;
-        cached[dev].store(cus, std::memory_order_relaxed);
-    }
-    *out = cus;
-    return hipSuccess;
-}
-
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs &a, hipStream_t stream) {
     int cus = 0;
-    const hipError_t e = cu_count(&cus);
+    const hipError_t e = device_cu_count(&cus);
     if (e != hipSuccess) return e;
     const long long two_per_cu = 2LL * cus;
     // 8-wave workgroups of 256 rows of one head when the rows see similar
@@ -514,6 +496,24 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Compute units of the current device, queried once per device.
+hipError_t device_cu_count(int *out) {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    int cus = cached[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        cus = cus > 0 ? cus : 1;
+        cached[dev].store(cus, std::memory_order_relaxed);
+    }
+    *out = cus;
+    return hipSuccess;
+}
 
 hipError_t launch_prefill_bf16(const FwdArgs &a, hipStream_t stream) {
     if (a.d == 128) return a.causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);

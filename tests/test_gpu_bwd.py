@@ -172,3 +172,22 @@ def test_bwd_workload_sampled(orc, name):
     check_grad("%s dq (%d rows)" % (name, len(qrows)), dq[qrows[:, 0], qrows[:, 1], qrows[:, 2]], rq)
     check_grad("%s dk (%d rows)" % (name, len(krows)), dk[krows[:, 0], krows[:, 1], krows[:, 2]], rk)
     check_grad("%s dv (%d rows)" % (name, len(krows)), dv[krows[:, 0], krows[:, 1], krows[:, 2]], rv)
+
+
+@pytest.mark.parametrize("Nq,Nk,Hkv", [(583, 601, 16), (600, 650, 32)])
+def test_dq_workgroup_forms_agree(Nq, Nk, Hkv):
+    """On causal layers with many query heads the dq kernel runs 8-wave
+    workgroups over the same query positions of 8 heads (group of 8) or 4
+    heads (group of 4) that share a K/V head; one head alone is too small a
+    grid for that and runs 4-wave workgroups of 128 rows.  Each row's
+    arithmetic is the same in both forms, so dq must agree bit for bit."""
+    B, Hq, d = 2, 128, 128
+    q, k, v, do = I.bwd_inputs(B, Hq, Hkv, Nq, Nk, d, "bf16", seed=91 + Nq)
+    dq_all = gpu_fwd_bwd(q, k, v, do, 0.09, True)[0]
+    G = Hq // Hkv
+    for b, h in [(0, 0), (1, 37), (1, Hq - 1)]:
+        hk = h // G
+        say("[bwd forms] b=%d h=%d" % (b, h))
+        dq1 = gpu_fwd_bwd(q[b:b + 1, h:h + 1], k[b:b + 1, hk:hk + 1], v[b:b + 1, hk:hk + 1], do[b:b + 1, h:h + 1],
+                          0.09, True)[0]
+        assert np.array_equal(dq1[0, 0], dq_all[b, h]), (b, h)
