@@ -211,7 +211,7 @@ def backward_line(E, A, I, dev, q, k, v, o, lse, w, steps=20, warmup=50):
     tf = fl / (ms * 1e-3) / 1e12
     return {"value": round(tf, 2), "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
             "avg_launch_ms": round(ms, 5), "flops_per_launch": fl,
-            "kernels": "bwd_pre_kernel<128> + bwd_dq_kernel<128,true> + bwd_dkdv_kernel<128,true>",
+            "kernels": "bwd_pre_kernel<128> + bwd_dq_kernel<128,true,8,8> + bwd_dkdv_kernel<128,true>",
             "note": "algorithmic FLOPs = 2.5x the forward's (S, dP, dV, dK, dQ products); the kernels "
                     "recompute S and dP once more for dQ"}
 
