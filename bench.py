@@ -23,7 +23,8 @@ workload in full, next to that workload's GPU time.  After the timed steps,
 `startup` gives the library load and each kernel's first (cold) call;
 `decode_graph` times the decode workload on its own, eager and replayed from a
 HIP graph, and `decode_paged` times it against a paged cache (block table over
-a shuffled pool); `chunked_prefill` (a 2048-token chunk over 8192 cached tokens,
+a shuffled pool), replayed from a HIP graph as well, since there the binding's
+per-call host work exceeds the kernel; `chunked_prefill` (a 2048-token chunk over 8192 cached tokens,
 causal bottom-right) and `cross_attention` (2048 queries over 4096 keys,
 non-causal) time attn_fwd on the two rectangular workloads the same way;
 `backward` times attn_bwd (all three kernels) on the prefill workload with the
@@ -110,37 +111,33 @@ def paged_decode_line(E, A, I, dev, block_size, reps=4, steps=20, warmup=50):
         k_p, v_p = pools[i % reps]
         E.attn_decode_paged(q, k_p, v_p, bt, sl_d, scale=wd.scale, o=o, lse=lse, workspace=ws)
 
-    ms = timed_ms(call, steps, warmup)
+    eager = timed_ms(call, steps, warmup)
+    ms = graph_ms(call, reps)
     by = A.decode_bytes(sl.tolist(), wd.Hq, wd.Hkv, wd.d, wd.dtype)
     return {"value": round(by / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "frac_hbm": round(by / (ms * 1e-3) / 1e9 /
-            PEAK_HBM_GBS, 4), "avg_launch_ms": round(ms, 5), "block_size": block_size,
+            PEAK_HBM_GBS, 4), "avg_launch_ms": round(ms, 5), "eager_ms": round(eager, 5), "block_size": block_size,
             "sum_seq_len": int(sl.sum()), "bytes_per_launch": by,
-            "note": "same shape and lengths as the decode workload, rows in a shuffled pool of blocks"}
+            "note": "same shape and lengths as the decode workload, rows in a shuffled pool of blocks; avg_launch_ms "
+                    "from a HIP graph of one call per pool replica replayed back to back (eager_ms: the same calls "
+                    "issued one by one from Python, where the binding's per-call host work exceeds the kernel)"}
 
 
-def decode_graph_line(E, A, I, dev, qd, sl, caches, od, lsed, ws, steps=40, warmup=20, replays=20):
-    """The decode step on its own: eager back-to-back calls, and the same
-    calls replayed from a HIP graph that holds one call per cache replica
-    (the form a serving loop runs them in)."""
+def graph_ms(call, n, replays=20):
+    """Average duration of call(0) .. call(n-1) captured in one HIP graph and
+    replayed `replays` times back to back: the kernels' own time, with no
+    host work between launches."""
     import torch
 
-    wd = I.WORKLOADS["C5"]
-
-    def call(i):
-        kc, vc = caches[i % len(caches)]
-        E.attn_decode(qd, kc, vc, sl, scale=wd.scale, o=od, lse=lsed, workspace=ws)
-
-    eager = timed_ms(call, steps, warmup)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):  # warm-up off the default stream before capture
-        for i in range(len(caches)):
+        for i in range(n):
             call(i)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for i in range(len(caches)):
+        for i in range(n):
             call(i)
     for _ in range(5):
         g.replay()
@@ -151,7 +148,21 @@ def decode_graph_line(E, A, I, dev, qd, sl, caches, od, lsed, ws, steps=40, warm
         g.replay()
     t1.record()
     torch.cuda.synchronize()
-    graph = t0.elapsed_time(t1) / (replays * len(caches))
+    return t0.elapsed_time(t1) / (replays * n)
+
+
+def decode_graph_line(E, A, I, dev, qd, sl, caches, od, lsed, ws, steps=40, warmup=20, replays=20):
+    """The decode step on its own: eager back-to-back calls, and the same
+    calls replayed from a HIP graph that holds one call per cache replica
+    (the form a serving loop runs them in)."""
+    wd = I.WORKLOADS["C5"]
+
+    def call(i):
+        kc, vc = caches[i % len(caches)]
+        E.attn_decode(qd, kc, vc, sl, scale=wd.scale, o=od, lse=lsed, workspace=ws)
+
+    eager = timed_ms(call, steps, warmup)
+    graph = graph_ms(call, len(caches), replays)
     by = A.decode_bytes(sl.cpu().tolist(), wd.Hq, wd.Hkv, wd.d, wd.dtype)
     return {"value": round(by / (graph * 1e-3) / 1e9, 1), "unit": "GB/s",
             "frac_hbm": round(by / (graph * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "graph_call_ms": round(graph, 5),

@@ -1,5 +1,5 @@
-"""The entry points under HIP graph capture.  A forward pass, a decode step and
-a backward pass captured in one graph, replayed several times with other
+"""The entry points under HIP graph capture.  A forward pass, a decode step
+(contiguous and paged cache) and a backward pass captured in one graph, replayed several times with other
 eager work and synchronisations between the replays, reproduce the eager
 results bit for bit on every replay.  (None of the launches records a memset;
 every output is written by the kernels.)"""
@@ -18,17 +18,23 @@ def test_graph_replays_match_eager():
     B, Hq, Hkv, N, d = 1, 8, 2, 700, 128
     q, k, v, do = (t.to(dev) for t in I.bwd_inputs(B, Hq, Hkv, N, N, d, "bf16", seed=71))
     sl, qd, kc, vc = (t.to(dev) for t in I.decode_inputs(4, 32, 8, 1024, 128, "bf16", seed=72, lo=1, hi=1024))
+    slp, qp, kp, vp, bt = (t.to(dev) for t in I.paged_decode_inputs(4, 32, 8, 128, 64, 16, "bf16", seed=73,
+                                                                    lo=1, hi=1024))
     ws_d = torch.empty(E.attn_decode_workspace_bytes(4, 32, 8, 1024, 128), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(E.attn_bwd_workspace_bytes(B, Hq, N), dtype=torch.uint8, device=dev)
 
-    def run(o, l, od, ld, dq, dk, dv):
+    ws_p = torch.empty_like(ws_d)
+
+    def run(o, l, od, ld, op, lp, dq, dk, dv):
         E.attn_fwd(q, k, v, scale=0.09, causal=True, o=o, lse=l)
         E.attn_decode(qd, kc, vc, sl, scale=0.088, o=od, lse=ld, workspace=ws_d)
+        E.attn_decode_paged(qp, kp, vp, bt, slp, scale=0.088, o=op, lse=lp, workspace=ws_p)
         E.attn_bwd(q, k, v, o, do, l, scale=0.09, causal=True, dq=dq, dk=dk, dv=dv, workspace=ws_b)
 
     def outputs():
         return (torch.empty_like(q), torch.empty(B, Hq, N, device=dev), torch.empty_like(qd),
-                torch.empty(4, 32, device=dev), torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+                torch.empty(4, 32, device=dev), torch.empty_like(qp), torch.empty(4, 32, device=dev),
+                torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
 
     ref = outputs()
     run(*ref)
@@ -44,7 +50,7 @@ def test_graph_replays_match_eager():
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         run(*got)
-    names = ["o", "lse", "o_dec", "lse_dec", "dq", "dk", "dv"]
+    names = ["o", "lse", "o_dec", "lse_dec", "o_paged", "lse_paged", "dq", "dk", "dv"]
     for rep in range(4):
         for t in got:
             t.zero_()
