@@ -23,8 +23,9 @@ workload in full, next to that workload's GPU time.  After the timed steps,
 `startup` gives the library load and each kernel's first (cold) call;
 `decode_graph` times the decode workload on its own, eager and replayed from a
 HIP graph, and `decode_paged` times it against a paged cache (block table over
-a shuffled pool), replayed from a HIP graph as well, since there the binding's
-per-call host work exceeds the kernel; `chunked_prefill` (a 2048-token chunk over 8192 cached tokens,
+a shuffled pool), replayed from a HIP graph as well (calls issued one by one
+from Python add the binding's host work and the per-dispatch cost);
+`chunked_prefill` (a 2048-token chunk over 8192 cached tokens,
 causal bottom-right) and `cross_attention` (2048 queries over 4096 keys,
 non-causal) time attn_fwd on the two rectangular workloads the same way;
 `backward` times attn_bwd (all three kernels) on the prefill workload with the
@@ -120,7 +121,7 @@ def paged_decode_line(E, A, I, dev, block_size, reps=4, steps=20, warmup=50):
             "sum_seq_len": int(sl.sum()), "bytes_per_launch": by,
             "note": "same shape and lengths as the decode workload, rows in a shuffled pool of blocks; avg_launch_ms "
                     "from a HIP graph of one call per pool replica replayed back to back (eager_ms: the same calls "
-                    "issued one by one from Python, where the binding's per-call host work exceeds the kernel)"}
+                    "issued one by one from Python, with the binding's host work and the per-dispatch cost on top)"}
 
 
 def graph_ms(call, n, replays=20):
@@ -254,9 +255,9 @@ OTHER_CONFIGS = ("C1", "C2a", "C2b", "C3a", "C3a'", "C3b")
 
 def other_configs_line(E, A, I, dev, steps=20, warmup=20):
     """attn_fwd on the smaller prefill shapes, each timed on its own: 10 calls
-    captured in a HIP graph and replayed (these kernels take less time than
-    the binding's per-call host work, so calls issued one by one from Python
-    would time the host; that figure is kept as eager_us)."""
+    captured in a HIP graph and replayed, so that neither the binding's host
+    work nor the per-dispatch cost is timed with these short kernels; calls
+    issued one by one from Python are kept as eager_us."""
     import torch
 
     out = {}
