@@ -174,14 +174,16 @@ def test_bwd_workload_sampled(orc, name):
     check_grad("%s dv (%d rows)" % (name, len(krows)), dv[krows[:, 0], krows[:, 1], krows[:, 2]], rv)
 
 
-@pytest.mark.parametrize("Nq,Nk,Hkv", [(583, 601, 16), (600, 650, 32)])
-def test_dq_workgroup_forms_agree(Nq, Nk, Hkv):
+@pytest.mark.parametrize("Nq,Nk,Hq,Hkv", [(583, 601, 128, 16), (600, 650, 128, 32), (583, 601, 128, 8),
+                                         (600, 650, 192, 16)])
+def test_dq_workgroup_forms_agree(Nq, Nk, Hq, Hkv):
     """On causal layers with many query heads the dq kernel runs 8-wave
     workgroups over the same query positions of 8 heads (group of 8) or 4
     heads (group of 4) that share a K/V head; one head alone is too small a
-    grid for that and runs 4-wave workgroups of 128 rows.  Each row's
-    arithmetic is the same in both forms, so dq must agree bit for bit."""
-    B, Hq, d = 2, 128, 128
+    grid for that and runs 4-wave workgroups of 128 rows; groups of 16 and 12
+    take two and three blocks of heads.  Each row's arithmetic is the same in
+    both forms, so dq must agree bit for bit."""
+    B, d = 2, 128
     q, k, v, do = I.bwd_inputs(B, Hq, Hkv, Nq, Nk, d, "bf16", seed=91 + Nq)
     dq_all = gpu_fwd_bwd(q, k, v, do, 0.09, True)[0]
     G = Hq // Hkv

@@ -151,17 +151,19 @@ def test_gqa_equals_repeated_mha(G):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-@pytest.mark.parametrize("causal,Nq,Nk,Hkv", [(False, 300, 520, 16), (True, 300, 700, 16), (True, 583, 601, 16),
-                                             (True, 600, 650, 32)])
-def test_wide_and_narrow_workgroups_agree(causal, Nq, Nk, Hkv):
+@pytest.mark.parametrize("causal,Nq,Nk,Hq,Hkv", [(False, 300, 520, 128, 16), (True, 300, 700, 128, 16),
+                                                (True, 583, 601, 128, 16), (True, 600, 650, 128, 32),
+                                                (True, 583, 601, 128, 8), (True, 600, 650, 192, 16)])
+def test_wide_and_narrow_workgroups_agree(causal, Nq, Nk, Hq, Hkv):
     """With many query heads the launch uses 8-wave workgroups: 256 rows of
     one head for non-causal and chunked-causal layers, and for causal layers
     with rows at very different depths the same 32 query positions of the 8
     heads that share a K/V head (group of 8), or 64 positions of 4 heads
-    (group of 4).  One head alone is too small a grid for any of them and
-    uses 128-row workgroups of 4 waves.  Each row's arithmetic is the same in
-    every form, so the outputs must agree bit for bit."""
-    B, Hq, d = 2, 128, 128
+    (group of 4); groups of 16 and 12 take two and three such blocks of
+    heads.  One head alone is too small a grid for any of them and uses
+    128-row workgroups of 4 waves.  Each row's arithmetic is the same in every
+    form, so the outputs must agree bit for bit."""
+    B, d = 2, 128
     q, k, v = I.prefill_inputs(B, Hq, Hkv, Nq, Nk, d, "bf16", seed=61 + Nq)
     o_all, l_all = gpu_fwd(q, k, v, 0.09, causal)
     G = Hq // Hkv
