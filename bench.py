@@ -357,7 +357,7 @@ def cpu_baseline(q, k, v, w, target_s, per_config=()):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(asked for --gpus %d)." % args.gpus, file=sys.stderr)
         sys.exit(2)
 

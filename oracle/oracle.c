@@ -35,7 +35,7 @@
  *        sec. 2.3: grouped-query attention, groups of query heads share one
  *        K/V head.
  *
- * Readings where the pages are silent (each is listed in the design doc):
+ * Readings where the pages are silent:
  *   - causal alignment for Nq != Nk is bottom-right: query row i sits at
  *     absolute position i + (Nk - Nq), so it sees keys j <= i + (Nk - Nq);
  *   - GQA groups are contiguous: KV head of query head h is h / (Hq / Hkv);
