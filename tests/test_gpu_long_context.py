@@ -55,3 +55,18 @@ def test_prefill_short_chunk_over_long_keys(orc, causal):
     assert_close("Nk=2^16 O (%d rows)" % len(rows), I.to_f64(og), o_ref, TOL_O["bf16"])
     assert_close("Nk=2^16 LSE", I.to_f64(lg), lse_ref, TOL_LSE)
     assert torch.isfinite(o.float()).all().item(), "non-finite output somewhere in the full tensor"
+
+
+def test_paged_decode_long_sequences(orc):
+    """Paged cache at block size 16: each 100k+-key sequence spans over 6000
+    pool blocks in shuffled order, so the wave's 64-entry page of the block
+    table is reloaded about a hundred times per sequence."""
+    bs = 16
+    sl, q, kp, vp, bt = I.paged_decode_inputs(2, 16, 4, 128, bs, LONG // bs, "bf16", seed=905, lo=100000, hi=LONG,
+                                              spare_blocks=5)
+    say("[paged-long] q%s pool%s table%s L=%s" % (tuple(q.shape), tuple(kp.shape), tuple(bt.shape), sl.tolist()))
+    o, lse = E.attn_decode_paged(dev(q), dev(kp), dev(vp), dev(bt), dev(sl), scale=128 ** -0.5)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = orc.decode_paged(I.to_f64(q), I.to_f64(kp), I.to_f64(vp), bt.numpy(), sl.numpy(), 128 ** -0.5)
+    assert_close("paged L>=1e5 O", I.to_f64(o), o_ref, TOL_O["bf16"])
+    assert_close("paged L>=1e5 LSE", I.to_f64(lse), lse_ref, TOL_LSE)
