@@ -17,9 +17,14 @@ The JSON line reports the prefill throughput in TFLOP/s as `value` (algorithmic
 FLOPs: 4*d per visible query/key pair), the decode bandwidth in GB/s (valid
 cache rows plus q, o, lse) in `decode`, and for each kernel its roofline
 fraction from its average duration measured with HIP events on the stream the
-kernels run on.  `cpu_baseline` times the fp64 oracle on a bounded sample of the
-prefill rows on the host cores, and (`per_config`) on each smaller prefill
-workload in full, next to that workload's GPU time.  After the timed steps,
+kernels run on (mean, with the median beside it).  `cpu_baseline` times the
+fp64 oracle on a bounded sample of the prefill rows on the host cores, and
+(`per_config`) on each smaller prefill workload in full, next to that
+workload's GPU time; `parity` compares the timed prefill's outputs with the
+oracle's on those sampled rows, `decode.parity` the timed decode's outputs on
+every row, and each `per_config` entry that workload's GPU outputs on every
+row (max-abs errors against the tolerances 1.5e-2 for bf16 O, 1e-5 for fp32
+O, 1e-3 for LSE).  After the timed steps,
 `startup` gives the library load and each kernel's first (cold) call;
 `decode_graph` times the decode workload on its own, eager and replayed from a
 HIP graph, and `decode_paged` times it against a paged cache (block table over
@@ -41,6 +46,7 @@ too small to fill the chip.
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -77,10 +83,11 @@ def parse():
     return ap.parse_args()
 
 
-def stored_traffic(kernel):
-    """Per-launch HBM bytes from the committed counter summary, or None when
-    it is absent or was taken on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def _stored(name, kernel, field):
+    """A per-kernel figure from a committed counter summary
+    (profiles/<name>.json), or None when it is absent or was taken on other
+    kernel sources."""
+    path = os.path.join(ROOT, "profiles", name + ".json")
     try:
         with open(path) as f:
             t = json.load(f)
@@ -91,7 +98,18 @@ def stored_traffic(kernel):
     e = t.get("kernels", {}).get(kernel)
     if e is None or e.get("source_digest") != source_digest(kernel):
         return None
-    return e.get("bytes_per_launch")
+    return e.get(field)
+
+
+def stored_traffic(kernel):
+    """Per-launch HBM bytes (FETCH_SIZE + WRITE_SIZE run), or None."""
+    return _stored("traffic", kernel, "bytes_per_launch")
+
+
+def stored_clock(kernel):
+    """The engine clock (GHz) the SQ counter run observed over the kernel
+    (SQ_CYCLES per shader engine over the dispatch duration), or None."""
+    return _stored("counters", kernel, "clock_ghz")
 
 
 def paged_decode_line(E, A, I, dev, block_size, reps=4, steps=20, warmup=50):
@@ -260,7 +278,7 @@ def other_configs_line(E, A, I, dev, steps=20, warmup=20):
     issued one by one from Python are kept as eager_us."""
     import torch
 
-    out = {}
+    out, outputs = {}, {}
     for name in OTHER_CONFIGS:
         w = I.WORKLOADS[name]
         causal = w.causal
@@ -280,7 +298,9 @@ def other_configs_line(E, A, I, dev, steps=20, warmup=20):
                      "us": round(ms * 1e3, 2), "eager_us": round(eager * 1e3, 2), "tflops": round(tf, 2),
                      "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4) if w.dtype == "bf16" else None,
                      "gbs": round(by / (ms * 1e-3) / 1e9, 1)}
-    return out
+        torch.cuda.synchronize()
+        outputs[name] = (o.cpu(), lse.cpu())
+    return out, outputs
 
 
 def cpu_model():
@@ -294,8 +314,27 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(q, k, v, w, target_s, per_config=()):
-    """The oracle, as it stands, on a bounded sample of prefill rows."""
+TOL_O = {"f32": 1e-5, "bf16": 1.5e-2}
+TOL_LSE = 1e-3
+
+
+def _max_abs(a, b):
+    """max |a - b| with equal infinities counting as equal (NaN if any NaN)."""
+    import numpy as np
+
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    same_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    with np.errstate(invalid="ignore"):
+        d = np.where(same_inf, 0.0, np.abs(a - b))
+    return float(d.max()) if d.size else 0.0
+
+
+def cpu_baseline(q, k, v, w, target_s, per_config=(), gpu_out=None, gpu_config_out=None):
+    """The oracle, as it stands, on a bounded sample of prefill rows.  With
+    gpu_out = (o, lse) of the timed prefill, the same rows are compared with
+    the oracle's (`parity`); gpu_config_out[name] = (o, lse) of each smaller
+    workload is compared with its full oracle run."""
     import numpy as np
 
     import oracle
@@ -323,7 +362,7 @@ def cpu_baseline(q, k, v, w, target_s, per_config=()):
     n = int(min(max(64, rows.shape[0] * max(target_s, 0.5) / max(dt, 1e-6)), w.Hq * w.N))
     rows = sample(n)
     t0 = time.perf_counter()
-    oracle.attn_rows(qd, kd, vd, w.scale, w.causal, rows, nthreads=nthreads)
+    o_ref, lse_ref = oracle.attn_rows(qd, kd, vd, w.scale, w.causal, rows, nthreads=nthreads)
     dt = time.perf_counter() - t0
     f = flops(rows)
     res = {
@@ -337,6 +376,14 @@ def cpu_baseline(q, k, v, w, target_s, per_config=()):
                   % (n, f / 1e9, 4.0 * w.d * w.Hq * w.N * (w.N + 1) / 2 / 1e9, dt, rate / 1e9),
         "seconds": dt,
     }
+    if gpu_out is not None:
+        o_gpu, lse_gpu = gpu_out
+        sel = (rows[:, 0], rows[:, 1], rows[:, 2])
+        eo = _max_abs(I.to_f64(o_gpu[sel]), o_ref)
+        el = _max_abs(I.to_f64(lse_gpu[sel]), lse_ref)
+        res["parity"] = {"rows": int(n), "max_abs_o": eo, "max_abs_lse": el, "tol_o": TOL_O[w.dtype],
+                         "tol_lse": TOL_LSE, "within_tol": bool(eo <= TOL_O[w.dtype] and el <= TOL_LSE),
+                         "note": "the timed prefill's o and lse on the oracle's sampled rows"}
     if per_config:
         # the smaller prefill configs in full, for the oracle's wall time next
         # to the GPU's (a few seconds together)
@@ -346,12 +393,30 @@ def cpu_baseline(q, k, v, w, target_s, per_config=()):
             c = I.WORKLOADS[name]
             cq, ck, cv = [I.to_f64(t) for t in I.workload_inputs(name)]
             t0 = time.perf_counter()
-            oracle.attn(cq, ck, cv, c.scale, c.causal, nthreads=nthreads)
+            co, cl = oracle.attn(cq, ck, cv, c.scale, c.causal, nthreads=nthreads)
             cdt = time.perf_counter() - t0
             cf = A.prefill_flops(c.B, c.Hq, c.Nq, c.Nkv, c.d, c.causal)
             per[name] = {"seconds": round(cdt, 4), "gflop": round(cf / 1e9, 3), "gflops": round(cf / cdt / 1e9, 1)}
+            if gpu_config_out and name in gpu_config_out:
+                go, gl = gpu_config_out[name]
+                eo, el = _max_abs(I.to_f64(go), co), _max_abs(I.to_f64(gl), cl)
+                per[name].update({"max_abs_o": eo, "max_abs_lse": el,
+                                  "within_tol": bool(eo <= TOL_O[c.dtype] and el <= TOL_LSE)})
         res["per_config"] = per
     return res
+
+
+def decode_parity(sl, q, kc, vc, o, lse, w):
+    """The timed decode's o and lse against the oracle on the whole workload."""
+    import oracle
+    from exact_scaled_dot_sdpa_amd import inputs as I
+
+    o_ref, lse_ref = oracle.decode(I.to_f64(q), I.to_f64(kc), I.to_f64(vc), sl.numpy(), w.scale)
+    eo, el = _max_abs(I.to_f64(o), o_ref), _max_abs(I.to_f64(lse), lse_ref)
+    return {"rows": int(o_ref.shape[0] * o_ref.shape[1]), "max_abs_o": eo, "max_abs_lse": el,
+            "tol_o": TOL_O[w.dtype], "tol_lse": TOL_LSE,
+            "within_tol": bool(eo <= TOL_O[w.dtype] and el <= TOL_LSE),
+            "note": "the timed decode's o and lse (last step) against the oracle, every row"}
 
 
 def main():
@@ -452,9 +517,15 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    p_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    d_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    p_all = [e[0].elapsed_time(e[1]) for e in ev]
+    d_all = [e[1].elapsed_time(e[2]) for e in ev]
+    p_ms, d_ms = sum(p_all) / K, sum(d_all) / K
+    p_med, d_med = statistics.median(p_all), statistics.median(d_all)
     ms_per_step = wall * 1e3 / K
+    # the timed calls' outputs (every step writes the same values), for the
+    # parity check against the oracle after the other measurements
+    timed_prefill = (o.cpu(), lse.cpu()) if run_p else None
+    timed_decode = (od.cpu(), lsed.cpu()) if run_d else None
 
     p_tflops = p_flops / (p_ms * 1e-3) / 1e12 if run_p else None
     d_gbs = d_bytes / (d_ms * 1e-3) / 1e9 if run_d else None
@@ -476,8 +547,8 @@ def main():
             "workload": "GQA causal prefill B=1 Hq=64 Hkv=8 N=8192 d=128 bf16 + KV-cache decode B=16 "
                         "Hq=32 Hkv=8 d=128 bf16 L~U[512,4096]",
             "prefill": {"B": wp.B, "Hq": wp.Hq, "Hkv": wp.Hkv, "N": wp.N, "d": wp.d, "causal": wp.causal,
-                        "flops_per_launch": p_flops, "bytes_per_launch": p_bytes},
-            "decode": {"B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "Lmax": wd.Lmax, "d": wd.d,
+                        "seed": wp.seed, "flops_per_launch": p_flops, "bytes_per_launch": p_bytes},
+            "decode": {"B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "Lmax": wd.Lmax, "d": wd.d, "seed": wd.seed,
                        "sum_seq_len": int(sl_cpu.sum()), "bytes_per_launch": d_bytes,
                        "flops_per_launch": d_flops, "cache_replicas": N_REPLICAS},
             "parallelism": "single GPU",
@@ -489,16 +560,21 @@ def main():
             "bound": "mfma", "achieved": round(p_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4), "traffic": tr,
             "kernel": "prefill_bf16_kernel<128,true,8,8>", "avg_launch_ms": round(p_ms, 5),
+            "median_launch_ms": round(p_med, 5),
+            "median_tflops": round(p_flops / (p_med * 1e-3) / 1e12, 2),
+            "sclk_ghz_counters": stored_clock("prefill"),
         }
     if run_d:
         tr = stored_traffic("decode")
         out["decode"] = {"value": round(d_gbs, 1), "unit": "GB/s", "frac_hbm": round(d_gbs / PEAK_HBM_GBS, 4),
-                         "avg_launch_ms": round(d_ms, 5),
+                         "avg_launch_ms": round(d_ms, 5), "median_launch_ms": round(d_med, 5),
+                         "median_gbs": round(d_bytes / (d_med * 1e-3) / 1e9, 1),
                          "tflops": round(d_flops / (d_ms * 1e-3) / 1e12, 2)}
         out["roofline_decode"] = {
             "bound": "hbm", "achieved": round(d_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(d_gbs / PEAK_HBM_GBS, 4), "traffic": tr,
             "kernel": "decode_chunk_kernel<128,4,3> + decode_merge_kernel<128>", "avg_launch_ms": round(d_ms, 5),
+            "median_launch_ms": round(d_med, 5),
         }
     out["startup"] = dict(startup, note="library load and the first call of each kernel (code-object load "
                           "included), against the warm per-call times above; compilation happens at build time")
@@ -513,14 +589,19 @@ def main():
         out["backward"] = backward_line(E, A, I, dev, q, k, v, o, lse, wp)
     if run_8:
         out["fp8_prefill"] = fp8_prefill_line(E, A, I, dev)
+    config_outputs = None
     if run_p and not args.no_configs:
-        out["other_configs"] = other_configs_line(E, A, I, dev)
+        out["other_configs"], config_outputs = other_configs_line(E, A, I, dev)
     if run_p and not args.no_rect:
         out["chunked_prefill"] = rect_prefill_line(E, A, I, dev, "X1")
         out["cross_attention"] = rect_prefill_line(E, A, I, dev, "X2")
+    if not args.no_cpu_baseline and run_d:
+        out["decode"]["parity"] = decode_parity(sl_cpu, qd_cpu, kc_cpu, vc_cpu, *timed_decode, wd)
     if not args.no_cpu_baseline and run_p:
         out["cpu_baseline"] = cpu_baseline(q_cpu, k_cpu, v_cpu, wp, args.cpu_seconds,
-                                           per_config=() if args.no_configs else OTHER_CONFIGS)
+                                           per_config=() if args.no_configs else OTHER_CONFIGS,
+                                           gpu_out=timed_prefill, gpu_config_out=config_outputs)
+        out["parity"] = dict(out["cpu_baseline"]["parity"], config="C4")
         for name, rec in out["cpu_baseline"].get("per_config", {}).items():
             if name in out.get("other_configs", {}):
                 rec["gpu_us"] = out["other_configs"][name]["us"]

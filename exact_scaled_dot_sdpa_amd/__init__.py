@@ -10,10 +10,13 @@ Functions carry the names of the C entry points:
     attn_fwd(q, k, v, scale=None, causal=False, o=None, lse=None, return_lse=True)
     attn_fwd_fp8(q, k, v, scale=None, v_scale=1.0, causal=False, o=None, lse=None, return_lse=True)
     attn_decode(q, k_cache, v_cache, seq_lens, scale=None, o=None, lse=None,
-                workspace=None, keys_per_split=0, return_lse=True)
+                workspace=None, return_lse=True)
+    attn_decode_split(q, k_cache, v_cache, seq_lens, keys_per_split, scale=None, o=None,
+                      lse=None, workspace=None, return_lse=True)
     attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, o=None,
                       lse=None, workspace=None, keys_per_split=0, return_lse=True)
-    attn_decode_workspace_bytes(B, Hq, Hkv, max_seq_len, d, keys_per_split=0)
+    attn_decode_workspace_bytes(B, Hq, Hkv, max_seq_len, d)
+    attn_decode_split_workspace_bytes(B, Hq, Hkv, max_seq_len, d, keys_per_split)
     attn_bwd(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None, dv=None,
              workspace=None)
     attn_bwd_workspace_bytes(B, Hq, Nq)
@@ -35,6 +38,8 @@ from ._binding import (  # noqa: F401
     attn_bwd_workspace_bytes,
     attn_decode,
     attn_decode_paged,
+    attn_decode_split,
+    attn_decode_split_workspace_bytes,
     attn_decode_workspace_bytes,
     attn_fwd,
     attn_fwd_fp8,
@@ -48,7 +53,9 @@ __all__ = [
     "attn_fwd_fp8",
     "attn_decode",
     "attn_decode_paged",
+    "attn_decode_split",
     "attn_decode_workspace_bytes",
+    "attn_decode_split_workspace_bytes",
     "attn_bwd",
     "attn_bwd_workspace_bytes",
     "attn_status_str",

@@ -35,10 +35,14 @@ def lib():
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
     L.attn_fwd.restype = i
-    L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_decode_workspace_bytes.restype = sz
-    L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    L.attn_decode_split_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.attn_decode_split_workspace_bytes.restype = sz
+    L.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     L.attn_decode.restype = i
+    L.attn_decode_split.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    L.attn_decode_split.restype = i
     L.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp, sz, vp]
     L.attn_decode_paged.restype = i
     L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, i, vp]
@@ -199,14 +203,41 @@ def attn_bwd(q, k, v, o, dout, lse, scale=None, causal=False, dq=None, dk=None, 
     return dq, dk, dv
 
 
-def attn_decode_workspace_bytes(B, Hq, Hkv, max_seq_len, d, keys_per_split=0) -> int:
-    return int(lib().attn_decode_workspace_bytes(B, Hq, Hkv, max_seq_len, d, keys_per_split))
+def attn_decode_workspace_bytes(B, Hq, Hkv, max_seq_len, d) -> int:
+    return int(lib().attn_decode_workspace_bytes(B, Hq, Hkv, max_seq_len, d))
 
 
-def attn_decode(q, k_cache, v_cache, seq_lens, scale=None, o=None, lse=None, workspace=None,
-                keys_per_split=0, return_lse=True, stream=None):
-    """One decode step: q [B,Hq,d] against caches [B,Hkv,Lmax,d] (bf16) with
-    seq_lens int32 [B] on the device.  Returns (o, lse) or o."""
+def attn_decode_split_workspace_bytes(B, Hq, Hkv, max_seq_len, d, keys_per_split) -> int:
+    return int(lib().attn_decode_split_workspace_bytes(B, Hq, Hkv, max_seq_len, d, keys_per_split))
+
+
+def _decode_outputs(q, o, lse, return_lse):
+    """Caller-supplied or new o [B,Hq,d] (q's dtype) and lse fp32 [B,Hq]."""
+    torch = _torch()
+    B, Hq, _ = q.shape
+    if o is None:
+        o = torch.empty_like(q)
+    _check_dev("o", o, q.dtype)
+    if tuple(o.shape) != tuple(q.shape):
+        raise ValueError("o must have q's shape %s, got %s" % (tuple(q.shape), tuple(o.shape)))
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_dev("lse", lse, torch.float32)
+        if tuple(lse.shape) != (B, Hq):
+            raise ValueError("lse must be [B,Hq] = %s, got %s" % ((B, Hq), tuple(lse.shape)))
+    return o, lse
+
+
+def _workspace(workspace, need, device):
+    torch = _torch()
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    _check_dev("workspace", workspace)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _decode_shapes(q, k_cache, v_cache, seq_lens):
     torch = _torch()
     _check_dev("q", q)
     _check_dev("k_cache", k_cache, q.dtype)
@@ -218,26 +249,43 @@ def attn_decode(q, k_cache, v_cache, seq_lens, scale=None, o=None, lse=None, wor
     Bk, Hkv, Lmax, dk = k_cache.shape
     if Bk != B or dk != d or tuple(seq_lens.shape) != (B,):
         raise ValueError("decode shape mismatch")
+    return B, Hq, Hkv, Lmax, d
+
+
+def attn_decode(q, k_cache, v_cache, seq_lens, scale=None, o=None, lse=None, workspace=None, return_lse=True,
+                stream=None):
+    """One decode step: q [B,Hq,d] against caches [B,Hkv,Lmax,d] (bf16) with
+    seq_lens int32 [B] on the device.  Returns (o, lse) or o."""
+    B, Hq, Hkv, Lmax, d = _decode_shapes(q, k_cache, v_cache, seq_lens)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if o is None:
-        o = torch.empty_like(q)
-    _check_dev("o", o, q.dtype)
-    if lse is None and return_lse:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _check_dev("lse", lse, torch.float32)
-    need = attn_decode_workspace_bytes(B, Hq, Hkv, Lmax, d, keys_per_split)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    _check_dev("workspace", workspace)
-    ws_bytes = workspace.numel() * workspace.element_size()
+    o, lse = _decode_outputs(q, o, lse, return_lse)
+    workspace, ws_bytes = _workspace(workspace, attn_decode_workspace_bytes(B, Hq, Hkv, Lmax, d), q.device)
     st = lib().attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
                            o.data_ptr(), lse.data_ptr() if lse is not None else None,
-                           B, Hq, Hkv, Lmax, d, float(scale), int(keys_per_split), _dtype_code(q),
+                           B, Hq, Hkv, Lmax, d, float(scale), _dtype_code(q),
                            workspace.data_ptr(), ws_bytes, _stream_handle(q, stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode")
+    return (o, lse) if return_lse else o
+
+
+def attn_decode_split(q, k_cache, v_cache, seq_lens, keys_per_split, scale=None, o=None, lse=None, workspace=None,
+                      return_lse=True, stream=None):
+    """attn_decode with an explicit split: ranges of about keys_per_split keys
+    of the max_seq_len-sized cache (0: the default split)."""
+    B, Hq, Hkv, Lmax, d = _decode_shapes(q, k_cache, v_cache, seq_lens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o, lse = _decode_outputs(q, o, lse, return_lse)
+    need = attn_decode_split_workspace_bytes(B, Hq, Hkv, Lmax, d, keys_per_split)
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    st = lib().attn_decode_split(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+                                 o.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                 B, Hq, Hkv, Lmax, d, float(scale), int(keys_per_split), _dtype_code(q),
+                                 workspace.data_ptr(), ws_bytes, _stream_handle(q, stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_split")
     return (o, lse) if return_lse else o
 
 
@@ -262,18 +310,9 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, o=
     mb = block_table.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if o is None:
-        o = torch.empty_like(q)
-    _check_dev("o", o, q.dtype)
-    if lse is None and return_lse:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    if lse is not None:
-        _check_dev("lse", lse, torch.float32)
-    need = attn_decode_workspace_bytes(B, Hq, Hkv, mb * bs, d, keys_per_split)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    _check_dev("workspace", workspace)
-    ws_bytes = workspace.numel() * workspace.element_size()
+    o, lse = _decode_outputs(q, o, lse, return_lse)
+    need = attn_decode_split_workspace_bytes(B, Hq, Hkv, mb * bs, d, keys_per_split)
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
     st = lib().attn_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
                                  seq_lens.data_ptr(), o.data_ptr(), lse.data_ptr() if lse is not None else None,
                                  B, Hq, Hkv, nb, bs, mb, d, float(scale), int(keys_per_split), _dtype_code(q),

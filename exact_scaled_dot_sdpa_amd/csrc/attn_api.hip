@@ -55,8 +55,13 @@ void workspace_layout(const DecodePlan &p, int d, size_t *o_bytes, size_t *total
     *total = ob + rows * sizeof(float);
 }
 
+// Every size is at least 1 and query heads form whole groups.
+bool fwd_sizes_ok(int B, int Hq, int Hkv, int Nq, int Nk) {
+    return B >= 1 && Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0 && Nq >= 1 && Nk >= 1;
+}
+
 bool decode_sizes_ok(int B, int Hq, int Hkv, int max_seq_len) {
-    return B >= 0 && Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0 && max_seq_len >= 0;
+    return B >= 1 && Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0 && max_seq_len >= 1;
 }
 
 }  // namespace
@@ -64,18 +69,15 @@ bool decode_sizes_ok(int B, int Hq, int Hkv, int max_seq_len) {
 extern "C" {
 
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int Nq,
-             int Nk, int d, float scale, int causal, int dtype, hipStream_t stream)
+             int Nk, int d, float scale, int causal, attn_dtype_t dtype, hipStream_t stream)
 {
-    if (B < 0 || Nq < 0 || Nk < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+    if (!fwd_sizes_ok(B, Hq, Hkv, Nq, Nk)) return ATTN_ERR_INVALID_ARG;
     if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
     if (causal && Nq > Nk) return ATTN_ERR_INVALID_ARG;
     if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;
-    if (B == 0 || Nq == 0) return ATTN_OK;  // nothing to compute
-    if (!q || !o) return ATTN_ERR_INVALID_ARG;
-    if (Nk > 0 && (!k || !v)) return ATTN_ERR_INVALID_ARG;
-    if (!aligned(q, 16) || !aligned(o, 16) || (k && !aligned(k, 16)) || (v && !aligned(v, 16)))
-        return ATTN_ERR_INVALID_ARG;
+    if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k, 16) || !aligned(v, 16)) return ATTN_ERR_INVALID_ARG;
     if (lse && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARG;
     // every index stays in 32-bit row counts: B*H*N rows, d columns
     if ((long long)B * Hq * Nq > 0x7fffffffLL || (long long)B * Hkv * Nk > 0x7fffffffLL)
@@ -90,15 +92,12 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
 int attn_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv, int Nq,
                  int Nk, int d, float scale, float v_scale, int causal, hipStream_t stream)
 {
-    if (B < 0 || Nq < 0 || Nk < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+    if (!fwd_sizes_ok(B, Hq, Hkv, Nq, Nk)) return ATTN_ERR_INVALID_ARG;
     if (!isfinite(scale) || !isfinite(v_scale)) return ATTN_ERR_INVALID_ARG;
     if (causal && Nq > Nk) return ATTN_ERR_INVALID_ARG;
     if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;
-    if (B == 0 || Nq == 0) return ATTN_OK;
-    if (!q || !o) return ATTN_ERR_INVALID_ARG;
-    if (Nk > 0 && (!k || !v)) return ATTN_ERR_INVALID_ARG;
-    if (!aligned(q, 16) || !aligned(o, 16) || (k && !aligned(k, 16)) || (v && !aligned(v, 16)))
-        return ATTN_ERR_INVALID_ARG;
+    if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k, 16) || !aligned(v, 16)) return ATTN_ERR_INVALID_ARG;
     if (lse && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARG;
     if ((long long)B * Hq * Nq > 0x7fffffffLL || (long long)B * Hkv * Nk > 0x7fffffffLL)
         return ATTN_ERR_UNSUPPORTED;
@@ -108,33 +107,29 @@ int attn_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *ls
 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq)
 {
-    if (B < 0 || Hq < 1 || Nq < 0) return 0;
+    if (B < 1 || Hq < 1 || Nq < 1) return 0;
     return (size_t)B * Hq * Nq * 2 * sizeof(float);
 }
 
 int attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout, const float *lse,
              void *dq, void *dk, void *dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
-             int dtype, void *workspace, size_t workspace_bytes, hipStream_t stream)
+             attn_dtype_t dtype, void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    if (B < 0 || Nq < 0 || Nk < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+    if (!fwd_sizes_ok(B, Hq, Hkv, Nq, Nk)) return ATTN_ERR_INVALID_ARG;
     if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
     if (causal && Nq > Nk) return ATTN_ERR_INVALID_ARG;
     if (!supported_d(d) || dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-    if (B == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
     if ((long long)B * Hq * Nq > 0x7fffffffLL || (long long)B * Hkv * Nk > 0x7fffffffLL)
         return ATTN_ERR_UNSUPPORTED;
-    // every tensor the kernels touch must be present and 16-byte aligned
-    // (q and do are also read for dk / dv, k and v also for dq)
-    const bool rows_q = Nq > 0, rows_k = Nk > 0;
-    if (rows_q && (!q || !o || !dout || !dq || !lse)) return ATTN_ERR_INVALID_ARG;
-    if (rows_k && (!k || !v || !dk || !dv)) return ATTN_ERR_INVALID_ARG;
+    // every tensor the kernels touch must be present and aligned (q and do
+    // are also read for dk / dv, k and v also for dq)
     const void *p16[] = {q, k, v, o, dout, dq, dk, dv};
     for (const void *p : p16)
-        if (p && !aligned(p, 16)) return ATTN_ERR_INVALID_ARG;
-    if (lse && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARG;
+        if (!p || !aligned(p, 16)) return ATTN_ERR_INVALID_ARG;
+    if (!lse || !aligned(lse, 4)) return ATTN_ERR_INVALID_ARG;
     const size_t need = attn_bwd_workspace_bytes(B, Hq, Nq);
-    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return ATTN_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_ERR_WORKSPACE;
 
     attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float *)workspace, B, Hq, Hkv, Nq, Nk, d, scale,
                     causal ? 1 : 0};
@@ -142,12 +137,17 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const v
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
-size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_seq_len, int d, int keys_per_split)
+size_t attn_decode_split_workspace_bytes(int B, int Hq, int Hkv, int max_seq_len, int d, int keys_per_split)
 {
     if (!decode_sizes_ok(B, Hq, Hkv, max_seq_len) || !supported_d(d) || keys_per_split < 0) return 0;
     size_t ob, total;
     workspace_layout(decode_plan(B, Hq, Hkv, max_seq_len, keys_per_split), d, &ob, &total);
     return total;
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_seq_len, int d)
+{
+    return attn_decode_split_workspace_bytes(B, Hq, Hkv, max_seq_len, d, 0);
 }
 
 }  // extern "C"
@@ -157,7 +157,7 @@ namespace {
 // Shared body of attn_decode and attn_decode_paged; the paged cache passes
 // block_table != nullptr and Lmax = max_blocks * block_size.
 int decode_call(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens, void *o, float *lse,
-                int B, int Hq, int Hkv, int Lmax, int d, float scale, int keys_per_split, int dtype,
+                int B, int Hq, int Hkv, int Lmax, int d, float scale, int keys_per_split, attn_dtype_t dtype,
                 void *workspace, size_t workspace_bytes, hipStream_t stream, const int32_t *block_table,
                 int block_size, int max_blocks, int num_blocks)
 {
@@ -166,16 +166,19 @@ int decode_call(const void *q, const void *k_cache, const void *v_cache, const i
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
     if (keys_per_split < 0) return ATTN_ERR_INVALID_ARG;
     if (!supported_d(d) || dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-    if (B == 0) return ATTN_OK;
-    if (!q || !o || !seq_lens || (Lmax > 0 && (!k_cache || !v_cache))) return ATTN_ERR_INVALID_ARG;
-    if (!aligned(q, 16) || !aligned(o, 16) || !aligned(seq_lens, 4) || (k_cache && !aligned(k_cache, 16)) ||
-        (v_cache && !aligned(v_cache, 16)))
+    if (!q || !o || !seq_lens || !k_cache || !v_cache) return ATTN_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(o, 16) || !aligned(seq_lens, 4) || !aligned(k_cache, 16) ||
+        !aligned(v_cache, 16))
         return ATTN_ERR_INVALID_ARG;
     if (lse && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARG;
     const DecodePlan p = decode_plan(B, Hq, Hkv, Lmax, keys_per_split);
-    // cache rows and segment counts stay in 32-bit arithmetic
+    // cache rows, segment counts and the kernels' sums of 64 sequence
+    // lengths stay in 32-bit arithmetic
     const long long rows = block_table ? (long long)num_blocks * Hkv * block_size : (long long)B * Hkv * Lmax;
-    if (rows > 0x7fffffffLL || (long long)B * Hq > 0x7fffffffLL || p.slots > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+    const long long page_keys = (long long)(B < 64 ? B : 64) * Lmax;
+    if (rows > 0x7fffffffLL || page_keys > 0x7fffffffLL || (long long)B * Hq > 0x7fffffffLL ||
+        p.slots > 0x7fffffffLL)
+        return ATTN_ERR_UNSUPPORTED;
     size_t ob, need;
     workspace_layout(p, d, &ob, &need);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_ERR_WORKSPACE;
@@ -192,8 +195,16 @@ int decode_call(const void *q, const void *k_cache, const void *v_cache, const i
 extern "C" {
 
 int attn_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens, void *o,
-                float *lse, int B, int Hq, int Hkv, int max_seq_len, int d, float scale, int keys_per_split,
-                int dtype, void *workspace, size_t workspace_bytes, hipStream_t stream)
+                float *lse, int B, int Hq, int Hkv, int max_seq_len, int d, float scale, attn_dtype_t dtype,
+                void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return decode_call(q, k_cache, v_cache, seq_lens, o, lse, B, Hq, Hkv, max_seq_len, d, scale, 0, dtype,
+                       workspace, workspace_bytes, stream, nullptr, 0, 0, 0);
+}
+
+int attn_decode_split(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens, void *o,
+                      float *lse, int B, int Hq, int Hkv, int max_seq_len, int d, float scale, int keys_per_split,
+                      attn_dtype_t dtype, void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     return decode_call(q, k_cache, v_cache, seq_lens, o, lse, B, Hq, Hkv, max_seq_len, d, scale, keys_per_split,
                        dtype, workspace, workspace_bytes, stream, nullptr, 0, 0, 0);
@@ -201,18 +212,16 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, const i
 
 int attn_decode_paged(const void *q, const void *k_pages, const void *v_pages, const int32_t *block_table,
                       const int32_t *seq_lens, void *o, float *lse, int B, int Hq, int Hkv, int num_blocks,
-                      int block_size, int max_blocks_per_seq, int d, float scale, int keys_per_split, int dtype,
-                      void *workspace, size_t workspace_bytes, hipStream_t stream)
+                      int block_size, int max_blocks_per_seq, int d, float scale, int keys_per_split,
+                      attn_dtype_t dtype, void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    if (num_blocks < 0 || block_size < 1 || max_blocks_per_seq < 0) return ATTN_ERR_INVALID_ARG;
+    if (num_blocks < 1 || block_size < 1 || max_blocks_per_seq < 1) return ATTN_ERR_INVALID_ARG;
     const long long lmax = (long long)max_blocks_per_seq * block_size;
     if (lmax > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
-    // an empty pool holds no rows: every sequence is empty
-    const int Lmax = num_blocks > 0 ? (int)lmax : 0;
-    if (Lmax > 0 && (!block_table || !aligned(block_table, 4))) return ATTN_ERR_INVALID_ARG;
-    return decode_call(q, k_pages, v_pages, seq_lens, o, lse, B, Hq, Hkv, Lmax, d, scale, keys_per_split, dtype,
-                       workspace, workspace_bytes, stream, Lmax > 0 ? block_table : nullptr, block_size,
-                       max_blocks_per_seq, num_blocks);
+    if (!block_table || !aligned(block_table, 4)) return ATTN_ERR_INVALID_ARG;
+    return decode_call(q, k_pages, v_pages, seq_lens, o, lse, B, Hq, Hkv, (int)lmax, d, scale, keys_per_split,
+                       dtype, workspace, workspace_bytes, stream, block_table, block_size, max_blocks_per_seq,
+                       num_blocks);
 }
 
 const char *attn_status_str(int status)

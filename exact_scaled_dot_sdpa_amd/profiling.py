@@ -45,9 +45,10 @@ def _short(name):
     return name[:60]
 
 
-def _last_n_means(trace_csv, n):
-    """Average duration (us) of the last n dispatches of each kernel in a
-    rocprofv3 kernel_trace csv (the timed steps, after the warm-up ones)."""
+def _last_n(trace_csv, n):
+    """(dispatches, median us, mean us) of the last n dispatches of each
+    kernel in a rocprofv3 kernel_trace csv (the timed steps, after the
+    warm-up ones)."""
     per = {}
     for r in csv.DictReader(open(trace_csv)):
         per.setdefault(r["Kernel_Name"], []).append(
@@ -56,7 +57,7 @@ def _last_n_means(trace_csv, n):
     for name, v in per.items():
         v.sort()
         last = [d for _, d in v[-n:]]
-        res[name] = (len(last), sum(last) / len(last) / 1e3)
+        res[name] = (len(last), statistics.median(last) / 1e3, sum(last) / len(last) / 1e3)
     return res
 
 
@@ -69,12 +70,13 @@ def stats(path, cmd, out, trace=None, last=0):
             _short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
     if trace and last > 0:
-        means = _last_n_means(trace, last)
-        lines += ["", "Average over the last %d dispatches of each kernel (the timed steps; the table above "
-                      "also counts the warm-up dispatches):" % last, "",
-                  "| kernel | dispatches | avg (us) |", "|---|---|---|"]
-        for name, (cnt, avg) in sorted(means.items(), key=lambda kv: -kv[1][1]):
-            lines.append("| %s | %d | %.2f |" % (_short(name), cnt, avg))
+        timed = _last_n(trace, last)
+        lines += ["", "The last %d dispatches of each kernel (the timed steps; the table above also counts the "
+                      "warm-up dispatches), from the kernel trace: the median is the primary figure, the mean "
+                      "the one the bench line's HIP events compare with:" % last, "",
+                  "| kernel | dispatches | median (us) | mean (us) |", "|---|---|---|---|"]
+        for name, (cnt, med, avg) in sorted(timed.items(), key=lambda kv: -kv[1][2]):
+            lines.append("| %s | %d | %.2f | %.2f |" % (_short(name), cnt, med, avg))
     lines += ["", "Full kernel names:", ""] + ["- `%s`" % r["Name"] for r in rows]
     text = "\n".join(lines) + "\n"
     with open(out, "w") as f:
@@ -163,11 +165,13 @@ N_SE, N_SIMD, MOP_FLOPS = 32, 1024, 512
 PEAK_BF16_TFLOPS, PEAK_FP8_TFLOPS, PEAK_CLOCK_GHZ = 2500.0, 5000.0, 2.4
 
 
-def counters(csv_path, cmd, out, algorithmic=None):
+def counters(csv_path, cmd, out, algorithmic=None, json_out=None):
     """Per-kernel medians over the dispatches of a --pmc run, with the derived
     figures: executed MFMA FLOPs against the algorithmic ones, the clock
     (cycles over duration), the share of SIMD cycles with the MFMA unit busy,
-    and the shares of wave time spent waiting."""
+    and the shares of wave time spent waiting.  With json_out, each logical
+    kernel's clock (its parts' cycles over their summed durations) and MFMA
+    busy share are stored with its source digest, for bench.py to report."""
     per = {}
     for r in csv.DictReader(open(csv_path)):
         k = _short(r["Kernel_Name"])
@@ -184,6 +188,7 @@ def counters(csv_path, cmd, out, algorithmic=None):
     derived = ["", "| kernel | duration (us) | clock (GHz) | MFMA busy | executed MFMA TFLOP | algorithmic TFLOP |"
                " algorithmic rate vs peak at this clock | wait share | wait-issue share |",
                "|---|---|---|---|---|---|---|---|---|"]
+    parts = {}  # short kernel name -> (cycles per engine, duration ns, MFMA busy cycles per SIMD)
     for k, ds in per.items():
         if k.startswith("__amd"):
             continue
@@ -194,6 +199,7 @@ def counters(csv_path, cmd, out, algorithmic=None):
                      + " |")
         cyc = med.get("SQ_CYCLES", 0.0) / N_SE
         clock = cyc / dur if dur > 0 else 0.0  # cycles per ns = GHz
+        parts[k] = (cyc, dur, med.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / N_SIMD)
         busy = med.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (N_SIMD * cyc) if cyc > 0 else 0.0
         mops = sum(v for c, v in med.items() if c.startswith("SQ_INSTS_VALU_MFMA_MOPS"))
         wc = med.get("SQ_WAVE_CYCLES", 0.0)
@@ -213,6 +219,20 @@ def counters(csv_path, cmd, out, algorithmic=None):
     text = "\n".join(lines + derived) + "\n"
     with open(out, "w") as f:
         f.write(text)
+    if json_out:
+        from exact_scaled_dot_sdpa_amd.build import source_digest
+
+        kernels = {}
+        for logical, names in KERNELS.items():
+            found = [parts[k] for k in parts if any(n in k for n in names)]
+            if len(found) != len(names) or not all(c > 0 and d > 0 for c, d, _ in found):
+                continue
+            cyc, dur, busy = (sum(x[i] for x in found) for i in range(3))
+            kernels[logical] = {"clock_ghz": round(cyc / dur, 3), "mfma_busy": round(busy / cyc, 4),
+                                "duration_us": round(dur / 1e3, 2), "source_digest": source_digest(logical)}
+        with open(json_out, "w") as f:
+            json.dump({"command": cmd, "kernels": kernels}, f, indent=1)
+            f.write("\n")
     return text
 
 
@@ -224,7 +244,8 @@ def main(argv=None):
     s.add_argument("--cmd", required=True)
     s.add_argument("--out", required=True)
     s.add_argument("--trace", default=None, help="kernel_trace csv of the same run")
-    s.add_argument("--last", type=int, default=0, help="also average the last N dispatches per kernel")
+    s.add_argument("--last", type=int, default=0,
+                   help="also give the median and mean of the last N dispatches per kernel")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -239,6 +260,7 @@ def main(argv=None):
     c.add_argument("--out", required=True)
     c.add_argument("--algorithmic", default=None,
                    help="kernel=FLOPs[,kernel=FLOPs...]: algorithmic FLOPs per launch to compare with")
+    c.add_argument("--json", default=None, help="also store each logical kernel's clock here")
     a = ap.parse_args(argv)
     if a.what == "stats":
         print(stats(a.csv, a.cmd, a.out, a.trace, a.last))
@@ -247,7 +269,7 @@ def main(argv=None):
         for item in (a.algorithmic.split(",") if a.algorithmic else []):
             k, v = item.split("=")
             alg[k] = float(v)
-        print(counters(a.csv, a.cmd, a.out, alg))
+        print(counters(a.csv, a.cmd, a.out, alg, a.json))
     else:
         print(traffic(a.fetch, a.write, a.calib_mib, a.cmd_fetch, a.cmd_write, a.json, a.out))
 

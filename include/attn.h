@@ -19,9 +19,10 @@
  *
  * Conventions shared by every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
- *     allocates nothing.  Its only global state is a per-device cache of device
- *     properties (compute-unit count, decode occupancy), filled atomically on
- *     first use; calls on different streams may run concurrently.
+ *     allocates nothing.  Its only global state is a per-device cache of two
+ *     device properties (compute-unit count, decode occupancy), written once
+ *     on first use with the value the runtime reports; it never changes a
+ *     result, and calls on different streams or threads may run concurrently.
  *   - Tensors are contiguous, row-major, head dim innermost, 16-byte aligned
  *     (lse and seq_lens: 4-byte aligned).
  *   - Calls are asynchronous on `stream` (NULL = the null stream) and return
@@ -29,8 +30,10 @@
  *   - Arguments are validated before any HIP runtime call; an invalid call
  *     returns a non-zero status and enqueues nothing.  No C++ exception
  *     crosses this interface.
+ *   - Every size (batch, heads, sequence lengths) must be >= 1.
  *   - LSE is the natural-log log-sum-exp of each row's visible scaled scores,
- *     fp32; a row that sees no key has O = 0 and LSE = -inf.
+ *     fp32; a decode row that sees no key (seq_lens[b] == 0) has O = 0 and
+ *     LSE = -inf.
  */
 #ifndef EXACT_SDPA_ATTN_H
 #define EXACT_SDPA_ATTN_H
@@ -46,19 +49,23 @@ extern "C" {
 typedef struct ihipStream_t *hipStream_t;
 
 /* Element type of q, k, v, o (and of the caches for decode). */
-enum { ATTN_F32 = 0, ATTN_BF16 = 1 };
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
 
-/* Status codes. */
-enum {
+/* Status codes (every entry point returns one of these as an int). */
+typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, non-finite scale */
     ATTN_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. d not 64/128) */
     ATTN_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or too small */
     ATTN_ERR_LAUNCH = 4       /* the HIP runtime reported an error at launch */
-};
+} attn_status_t;
 
 /*
- * attn_fwd -- prefill / self- or cross-attention forward, MHA or GQA.
+ * attn_fwd -- prefill / self- or cross-attention forward, MHA or GQA:
+ * O = softmax(scale * Q K^T [+ causal mask]) V row by row ("Transformer 架构的
+ * 数学与计算深度解析", sec. 2.2-2.4 for the operation, sec. 4.1 for the causal
+ * mask; computed with the online recurrence of its sec. 6.3 and of "从注意力到
+ * IO 感知执行", sec. 8, eqs. (1)-(2), never storing the score matrix).
  *
  *   q   [B, Hq,  Nq, d]   dtype          (read)
  *   k   [B, Hkv, Nk, d]   dtype          (read)
@@ -74,17 +81,17 @@ enum {
  * sees every key (chunked prefill and decode agree with full causal prefill).
  * causal requires Nq <= Nk.
  *
- * Sizes: B >= 0, Nq >= 0, Nk >= 0, Hq >= 1, Hkv >= 1, Hq % Hkv == 0,
- * d in {64, 128}.  B == 0 or Nq == 0 is a no-op; Nk == 0 (non-causal) gives
- * O = 0 and LSE = -inf.  dtype is ATTN_F32 or ATTN_BF16; accumulation is fp32
- * in both cases.
+ * Sizes: B, Hq, Hkv, Nq, Nk >= 1, Hq % Hkv == 0, d in {64, 128}, and
+ * B * Hq * Nq, B * Hkv * Nk < 2^31 (ATTN_ERR_UNSUPPORTED beyond).  Every row
+ * sees at least one key (causal: row i sees keys 0 .. i + Nk - Nq).  dtype is
+ * ATTN_F32 or ATTN_BF16; accumulation is fp32 in both cases.
  *
  * Returns ATTN_OK, or ATTN_ERR_INVALID_ARG / ATTN_ERR_UNSUPPORTED (nothing
  * launched), or ATTN_ERR_LAUNCH.
  */
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
              int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
-             int causal, int dtype, hipStream_t stream);
+             int causal, attn_dtype_t dtype, hipStream_t stream);
 
 /*
  * attn_fwd_fp8 -- attn_fwd for q, k, v stored as fp8 (OCP e4m3, E4M3FN: 1
@@ -150,9 +157,8 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
  * Sizes, head mapping, scale and causal alignment as attn_fwd.  Only
  * dtype == ATTN_BF16 is implemented (ATTN_F32 returns ATTN_ERR_UNSUPPORTED);
  * products take bf16 operands (the weights and ds rounded to nearest even)
- * with fp32 accumulation, and the gradients are rounded to bf16.  Nq == 0
- * gives dk = dv = 0; Nk == 0 gives dq = 0.  Tensors of an empty side may be
- * NULL.  The result is deterministic (no atomics).
+ * with fp32 accumulation, and the gradients are rounded to bf16.  The result
+ * is deterministic (no atomics).
  *
  * Returns ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED,
  * ATTN_ERR_WORKSPACE (nothing launched in these three cases) or
@@ -161,21 +167,19 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
 int attn_bwd(const void *q, const void *k, const void *v, const void *o,
              const void *dout, const float *lse, void *dq, void *dk, void *dv,
              int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
-             int causal, int dtype, void *workspace, size_t workspace_bytes,
-             hipStream_t stream);
+             int causal, attn_dtype_t dtype, void *workspace,
+             size_t workspace_bytes, hipStream_t stream);
 
 /*
  * attn_decode_workspace_bytes -- bytes of device workspace attn_decode needs
- * for these sizes and this keys_per_split (see attn_decode).  Layout:
- *   fp32 partial outputs  [S, min(G, 16), d]
- *   fp32 partial LSEs     [S, min(G, 16)]   (from the next 256-byte boundary)
- * with G = Hq / Hkv and S = B * Hkv * ceil(G / 16) + W - 1, where W is the
- * number of split workgroups: ceil(B * Hkv * ceil(G / 16) * max_seq_len /
- * keys_per_split) clamped to [1, 2048], or 2048 when keys_per_split is 0.
- * Returns 0 for invalid sizes.
+ * for these sizes: fp32 partial results of the split (see attn_decode),
+ *   partial outputs [S, min(G, 16), d], then (from the next 256-byte
+ *   boundary) partial LSEs [S, min(G, 16)],
+ * with G = Hq / Hkv and S = B * Hkv * ceil(G / 16) + 2047 slots.  Returns 0
+ * for sizes attn_decode would reject.
  */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_seq_len,
-                                   int d, int keys_per_split);
+                                   int d);
 
 /*
  * attn_decode -- one decode step per sequence against a KV cache.
@@ -194,24 +198,49 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_seq_len,
  *            must not share one workspace.
  *
  * Query head h of sequence b attends, without a mask, to the first
- * seq_lens[b] rows of K/V head h / (Hq / Hkv); this equals the last row of
- * causal attn_fwd over those rows.  The cache is not appended to.
- * The valid keys of all (sequence, K/V head, block of 16 query heads) are
- * laid end to end and cut into W equal ranges, one per workgroup; the
- * partial results of blocks that several ranges share are merged through
- * their log-sum-exps by a second kernel.  keys_per_split = 0 lets the library
- * pick W (as many workgroups as the device holds at once); a positive value
- * asks for ranges of about that many keys of the max_seq_len-sized cache.
- * Only dtype ATTN_BF16 is implemented; any Hq / Hkv is supported.
+ * seq_lens[b] rows of K/V head h / (Hq / Hkv) ("Transformer 笔记：注意力机制为
+ * 什么会变成系统问题", KV-cache section: the new token's query reads the
+ * cached keys and values); this equals the last row of causal attn_fwd over
+ * those rows.  The cache is not appended to.  The valid keys of all
+ * (sequence, K/V head, block of 16 query heads) are laid end to end and cut
+ * into equal ranges, one per workgroup, as many as the device holds at once;
+ * the partial results of blocks that several ranges share are merged through
+ * their log-sum-exps ("从注意力到 IO 感知执行", sec. 8, eqs. (1)-(2), applied
+ * to whole ranges).  A sequence with seq_lens[b] == 0 gets O = 0 and
+ * LSE = -inf.  Only dtype ATTN_BF16 is implemented (ATTN_F32 returns
+ * ATTN_ERR_UNSUPPORTED); any Hq / Hkv is supported.
  *
- * Sizes: B >= 0 (0 is a no-op), Hq >= 1, Hkv >= 1, Hq % Hkv == 0,
- * max_seq_len >= 0, d in {64, 128}, keys_per_split >= 0.
+ * Sizes: B, Hq, Hkv, max_seq_len >= 1, Hq % Hkv == 0, d in {64, 128},
+ * B * Hkv * max_seq_len < 2^31.
+ * Returns ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED,
+ * ATTN_ERR_WORKSPACE (nothing launched in these three cases) or
+ * ATTN_ERR_LAUNCH.
  */
 int attn_decode(const void *q, const void *k_cache, const void *v_cache,
                 const int32_t *seq_lens, void *o, float *lse, int B, int Hq,
                 int Hkv, int max_seq_len, int d, float scale,
-                int keys_per_split, int dtype, void *workspace,
-                size_t workspace_bytes, hipStream_t stream);
+                attn_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/*
+ * attn_decode_split_workspace_bytes / attn_decode_split -- attn_decode with
+ * an explicit split: keys_per_split > 0 asks for ranges of about that many
+ * keys of the max_seq_len-sized cache, i.e. W = ceil(B * Hkv * ceil(G / 16) *
+ * max_seq_len / keys_per_split) workgroups clamped to [1, 2048];
+ * keys_per_split == 0 is attn_decode's default (as many workgroups as the
+ * device holds at once).  The workspace then has S = B * Hkv * ceil(G / 16) +
+ * W - 1 slots (W = 2048 for keys_per_split == 0), laid out as for
+ * attn_decode.  Everything else is attn_decode's.  The result is the same up
+ * to the order of floating-point sums (split invariance).
+ */
+size_t attn_decode_split_workspace_bytes(int B, int Hq, int Hkv,
+                                         int max_seq_len, int d,
+                                         int keys_per_split);
+int attn_decode_split(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *seq_lens, void *o, float *lse, int B,
+                      int Hq, int Hkv, int max_seq_len, int d, float scale,
+                      int keys_per_split, attn_dtype_t dtype, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream);
 
 /*
  * attn_decode_paged -- attn_decode against a paged KV cache: each sequence's
@@ -223,28 +252,30 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache,
  *   k_pages, v_pages [num_blocks, Hkv, block_size, d]  dtype (read): the pool
  *   block_table      [B, max_blocks_per_seq] int32, device (read): logical
  *            block j of sequence b is pool block block_table[b][j]; entries
- *            outside [0, num_blocks) are clamped into it (no fault, no error)
+ *            outside [0, num_blocks) are clamped into it (no fault, no error).
+ *            Only row b of the table is read for sequence b, and only the
+ *            entries of its valid blocks are used.
  *   seq_lens [B] int32, device: clamped to [0, max_blocks_per_seq *
- *            block_size]; rows at or beyond seq_lens[b] are never read, and
- *            neither are table entries past the last valid row's block
- *   q, o, lse, scale, keys_per_split, dtype, stream: as for attn_decode.
- *   workspace: as for attn_decode, sized by attn_decode_workspace_bytes(B,
- *            Hq, Hkv, max_blocks_per_seq * block_size, d, keys_per_split).
+ *            block_size]; rows at or beyond seq_lens[b] are never read
+ *   q, o, lse, scale, dtype, stream: as for attn_decode.
+ *   keys_per_split: as for attn_decode_split (0 = the default split).
+ *   workspace: as for attn_decode, sized by attn_decode_split_workspace_bytes(
+ *            B, Hq, Hkv, max_blocks_per_seq * block_size, d, keys_per_split).
  *
  * Blocks may be shared between sequences (shared prefixes).  block_size is
  * any positive value; a multiple of 32 keeps every 32-key chunk whole.
- * num_blocks == 0 makes every sequence empty (O = 0, LSE = -inf).
- * Sizes: num_blocks >= 0, block_size >= 1, max_blocks_per_seq >= 0,
- * max_blocks_per_seq * block_size < 2^31, num_blocks * Hkv * block_size < 2^31;
- * otherwise as for attn_decode.
+ * Sizes: num_blocks, block_size, max_blocks_per_seq >= 1,
+ * max_blocks_per_seq * block_size < 2^31, num_blocks * Hkv * block_size < 2^31,
+ * min(B, 64) * max_blocks_per_seq * block_size < 2^31; otherwise as for
+ * attn_decode.
  */
 int attn_decode_paged(const void *q, const void *k_pages, const void *v_pages,
                       const int32_t *block_table, const int32_t *seq_lens,
                       void *o, float *lse, int B, int Hq, int Hkv,
                       int num_blocks, int block_size, int max_blocks_per_seq,
-                      int d, float scale, int keys_per_split, int dtype,
-                      void *workspace, size_t workspace_bytes,
-                      hipStream_t stream);
+                      int d, float scale, int keys_per_split,
+                      attn_dtype_t dtype, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *attn_status_str(int status);

@@ -30,8 +30,12 @@ def gpu_fwd(q, k, v, scale, causal):
 
 
 def gpu_decode(seq_lens, q, kc, vc, scale, keys_per_split=0):
-    o, lse = E.attn_decode(dev(q), dev(kc), dev(vc), dev(seq_lens.to(torch.int32)), scale=scale,
-                           keys_per_split=keys_per_split)
+    """attn_decode (default split), or attn_decode_split for keys_per_split > 0."""
+    if keys_per_split:
+        o, lse = E.attn_decode_split(dev(q), dev(kc), dev(vc), dev(seq_lens.to(torch.int32)), keys_per_split,
+                                     scale=scale)
+    else:
+        o, lse = E.attn_decode(dev(q), dev(kc), dev(vc), dev(seq_lens.to(torch.int32)), scale=scale)
     torch.cuda.synchronize()
     return I.to_f64(o), I.to_f64(lse)
 
@@ -53,6 +57,26 @@ def assert_close(name, got, ref, tol):
     assert e == e, "%s: NaN in the result" % name
     assert e <= tol, "%s: max-abs err %.3e > %.1e" % (name, e, tol)
     return e
+
+
+def assert_rel_per_group(name, got, ref, group_axes, rel=2.0 ** -6):
+    """Per group of outputs (the leading `group_axes` axes index a group:
+    a sequence, or a (batch, head) pair), max |got - ref| <= rel * max |ref|
+    of that group.  Over many keys softmax(QK^T)V shrinks towards 0 (about
+    sqrt(e / L) for L keys of N(0,1) values), so the absolute bf16 bound
+    alone would pass even an all-zero output; 2^-6 leaves room for the
+    output's bf16 rounding (2^-9 relative) plus the weights' (2^-9 relative
+    each, averaged over the keys) several times over."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    lead = got.shape[:group_axes]
+    g = got.reshape(int(np.prod(lead)), -1)
+    r = ref.reshape(int(np.prod(lead)), -1)
+    err = np.abs(g - r).max(axis=1)
+    top = np.abs(r).max(axis=1)
+    ratio = float((err / np.maximum(top, 1e-300)).max())
+    say("  %-40s max err / max|ref| per group %.3e (bound %.3e)" % (name, ratio, rel))
+    assert np.all(err <= rel * top), "%s: relative error %.3e > %.3e" % (name, ratio, rel)
 
 
 def grad_floors(orc, q, k, v, do, scale, causal):

@@ -24,10 +24,54 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert names == sorted(["attn_fwd", "attn_decode", "attn_decode_paged", "attn_decode_workspace_bytes",
+                            "attn_decode_split", "attn_decode_split_workspace_bytes",
                             "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_fp8", "attn_status_str"])
     lib = ctypes.CDLL(E.lib_path())
     for n in names:
         assert hasattr(lib, n), "libattn.so does not export %s" % n
+
+
+def _prototype(name):
+    """The declaration of `name` in include/attn.h, comments removed and
+    whitespace collapsed."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    m = re.search(r"[\w\s\*]*\b%s\s*\([^;]*\);" % name, text)
+    assert m, name
+    return " ".join(m.group(0).split())
+
+
+def _normalise(proto):
+    return re.sub(r"\s*([(),*])\s*", r"\1", " ".join(proto.split())).strip()
+
+
+# The boundary's four calls and its two enums, as the scope table writes them.
+SCOPE_PROTOTYPES = {
+    "attn_fwd": "int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, "
+                "int Hkv, int Nq, int Nk, int d, float scale, int causal, attn_dtype_t dtype, "
+                "hipStream_t stream);",
+    "attn_decode_workspace_bytes": "size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_seq_len, "
+                                   "int d);",
+    "attn_decode": "int attn_decode(const void* q, const void* k_cache, const void* v_cache, "
+                   "const int32_t* seq_lens, void* o, float* lse, int B, int Hq, int Hkv, int max_seq_len, int d, "
+                   "float scale, attn_dtype_t dtype, void* workspace, size_t workspace_bytes, "
+                   "hipStream_t stream);",
+    "attn_status_str": "const char* attn_status_str(int status);",
+}
+
+
+@pytest.mark.parametrize("name", sorted(SCOPE_PROTOTYPES))
+def test_boundary_prototypes_are_the_scope_tables(name):
+    assert _normalise(_prototype(name)) == _normalise(SCOPE_PROTOTYPES[name])
+
+
+def test_boundary_enums():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    m = re.search(r"typedef enum\s*\{([^}]*)\}\s*attn_dtype_t;", text)
+    assert m and _normalise(m.group(1)) == _normalise("ATTN_F32 = 0, ATTN_BF16 = 1")
+    m = re.search(r"typedef enum\s*\{([^}]*)\}\s*attn_status_t;", text)
+    assert m and _normalise(m.group(1)) == _normalise(
+        "ATTN_OK = 0, ATTN_ERR_INVALID_ARG = 1, ATTN_ERR_UNSUPPORTED = 2, ATTN_ERR_WORKSPACE = 3, "
+        "ATTN_ERR_LAUNCH = 4")
 
 
 def test_status_strings():
@@ -62,17 +106,23 @@ def fwd(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64, scale=0.1
     (dict(q=P + 2), E.ATTN_ERR_INVALID_ARG),            # misaligned
     (dict(v=P + 8), E.ATTN_ERR_INVALID_ARG),
     (dict(lse=P + 2), E.ATTN_ERR_INVALID_ARG),
-    (dict(B=0), E.ATTN_OK),                              # empty: no-op
-    (dict(Nq=0), E.ATTN_OK),
-    (dict(Nq=0, Nk=0, causal=1), E.ATTN_OK),
+    (dict(B=0), E.ATTN_ERR_INVALID_ARG),                 # every size >= 1
+    (dict(Nq=0), E.ATTN_ERR_INVALID_ARG),
+    (dict(Nk=0), E.ATTN_ERR_INVALID_ARG),
+    (dict(Nq=0, Nk=0, causal=1), E.ATTN_ERR_INVALID_ARG),
+    (dict(Nq=1 << 16, Hq=1 << 15, Hkv=1 << 15), E.ATTN_ERR_UNSUPPORTED),  # rows >= 2^31
 ])
 def test_fwd_validation(kw, status):
     assert fwd(**kw) == status
 
 
-def dec(q=P, kc=P, vc=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Lmax=512, d=128, scale=0.09, kps=0, dtype=1,
+def dec(q=P, kc=P, vc=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Lmax=512, d=128, scale=0.09, kps=None, dtype=1,
         ws=P, ws_bytes=1 << 30):
-    return E.lib().attn_decode(q, kc, vc, sl, o, lse, B, Hq, Hkv, Lmax, d, scale, kps, dtype, ws, ws_bytes, None)
+    """attn_decode, or attn_decode_split when kps is given."""
+    if kps is None:
+        return E.lib().attn_decode(q, kc, vc, sl, o, lse, B, Hq, Hkv, Lmax, d, scale, dtype, ws, ws_bytes, None)
+    return E.lib().attn_decode_split(q, kc, vc, sl, o, lse, B, Hq, Hkv, Lmax, d, scale, kps, dtype, ws, ws_bytes,
+                                     None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -80,7 +130,6 @@ def dec(q=P, kc=P, vc=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Lmax=512, d=128, sc
     (dict(B=-1), E.ATTN_ERR_INVALID_ARG),
     (dict(Lmax=-1), E.ATTN_ERR_INVALID_ARG),
     (dict(scale=float("nan")), E.ATTN_ERR_INVALID_ARG),
-    (dict(kps=-1), E.ATTN_ERR_INVALID_ARG),
     (dict(dtype=0), E.ATTN_ERR_UNSUPPORTED),            # fp32 decode not implemented
     (dict(d=96), E.ATTN_ERR_UNSUPPORTED),
     (dict(sl=None), E.ATTN_ERR_INVALID_ARG),
@@ -90,7 +139,14 @@ def dec(q=P, kc=P, vc=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Lmax=512, d=128, sc
     (dict(ws=None), E.ATTN_ERR_WORKSPACE),
     (dict(ws_bytes=1024), E.ATTN_ERR_WORKSPACE),
     (dict(ws=P + 4), E.ATTN_ERR_WORKSPACE),
-    (dict(B=0), E.ATTN_OK),
+    (dict(B=0), E.ATTN_ERR_INVALID_ARG),                # every size >= 1
+    (dict(Lmax=0), E.ATTN_ERR_INVALID_ARG),
+    (dict(Hq=0, Hkv=0), E.ATTN_ERR_INVALID_ARG),
+    (dict(kc=None), E.ATTN_ERR_INVALID_ARG),
+    (dict(kps=-1), E.ATTN_ERR_INVALID_ARG),              # attn_decode_split
+    (dict(kps=100, B=0), E.ATTN_ERR_INVALID_ARG),
+    (dict(kps=100, ws_bytes=1024), E.ATTN_ERR_WORKSPACE),
+    (dict(B=1 << 16, Hkv=1 << 4, Hq=1 << 4, Lmax=1 << 12), E.ATTN_ERR_UNSUPPORTED),  # cache rows >= 2^31
 ])
 def test_decode_validation(kw, status):
     assert dec(**kw) == status
@@ -113,18 +169,24 @@ def _ws_bytes(B, Hq, Hkv, Lmax, d, kps):
 
 
 def test_decode_workspace_bytes():
-    f = E.attn_decode_workspace_bytes
-    for args in [(16, 32, 8, 4096, 128, 0), (16, 32, 8, 4096, 128, 1024), (1, 1, 1, 0, 64, 0),
+    f = E.attn_decode_split_workspace_bytes
+    for args in [(16, 32, 8, 4096, 128, 0), (16, 32, 8, 4096, 128, 1024), (1, 1, 1, 1, 64, 0),
                  (3, 6, 2, 100, 64, 0), (2, 64, 2, 777, 128, 100), (2, 40, 2, 300, 64, 7)]:
         assert f(*args) == _ws_bytes(*args), args
+    for args in [(16, 32, 8, 4096, 128), (3, 6, 2, 100, 64), (1, 1, 1, 1, 64)]:
+        assert E.attn_decode_workspace_bytes(*args) == _ws_bytes(*args, 0), args
     # 16 x 8 segments + 512 workgroups of 1024 keys - 1, four heads each
     assert f(16, 32, 8, 4096, 128, 1024) == 639 * 4 * 128 * 4 + 639 * 4 * 4
-    assert f(1, 3, 2, 100, 64) == 0                  # invalid sizes
-    assert f(1, 2, 1, 100, 96) == 0
+    assert E.attn_decode_workspace_bytes(1, 3, 2, 100, 64) == 0     # invalid sizes
+    assert E.attn_decode_workspace_bytes(1, 2, 1, 100, 96) == 0
+    assert E.attn_decode_workspace_bytes(0, 2, 1, 100, 64) == 0
+    assert E.attn_decode_workspace_bytes(1, 2, 1, 0, 64) == 0
     assert f(1, 2, 1, 100, 64, -1) == 0
     # exactly the workspace that size reports is accepted, one byte less is not
-    need = f(2, 8, 2, 512, 128)
+    need = E.attn_decode_workspace_bytes(2, 8, 2, 512, 128)
     assert dec(ws_bytes=need - 1) == E.ATTN_ERR_WORKSPACE
+    need = f(2, 8, 2, 512, 128, 64)
+    assert dec(kps=64, ws_bytes=need - 1) == E.ATTN_ERR_WORKSPACE
 
 
 def pdec(q=P, kp=P, vp=P, bt=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, nb=16, bs=32, mb=8, d=128, scale=0.09, kps=0,
@@ -147,7 +209,11 @@ def pdec(q=P, kp=P, vp=P, bt=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, nb=16, bs=32
     (dict(kp=None), E.ATTN_ERR_INVALID_ARG),
     (dict(ws=None), E.ATTN_ERR_WORKSPACE),
     (dict(ws_bytes=1024), E.ATTN_ERR_WORKSPACE),
-    (dict(B=0), E.ATTN_OK),
+    (dict(B=0), E.ATTN_ERR_INVALID_ARG),                # every size >= 1
+    (dict(nb=0), E.ATTN_ERR_INVALID_ARG),
+    (dict(mb=0), E.ATTN_ERR_INVALID_ARG),
+    (dict(kps=-1), E.ATTN_ERR_INVALID_ARG),
+    (dict(B=100, mb=1 << 16, bs=1 << 10, nb=4), E.ATTN_ERR_UNSUPPORTED),  # 64 sequences' keys >= 2^31
 ])
 def test_decode_paged_validation(kw, status):
     assert pdec(**kw) == status
@@ -159,6 +225,8 @@ def test_decode_paged_workspace_is_the_contiguous_one():
     here)."""
     need = E.attn_decode_workspace_bytes(2, 8, 2, 8 * 32, 128)
     assert pdec(ws_bytes=need - 1) == E.ATTN_ERR_WORKSPACE
+    need = E.attn_decode_split_workspace_bytes(2, 8, 2, 8 * 32, 128, 50)
+    assert pdec(kps=50, ws_bytes=need - 1) == E.ATTN_ERR_WORKSPACE
 
 
 def bwd(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, Hq=4, Hkv=2, Nq=64, Nk=64, d=128, scale=0.09,
@@ -189,9 +257,9 @@ def bwd(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, Hq=4, Hkv=2, Nq=
     (dict(ws=P + 4), E.ATTN_ERR_WORKSPACE),
     (dict(ws_bytes=1 * 4 * 64 * 8 - 1), E.ATTN_ERR_WORKSPACE),
     (dict(Nq=1 << 16, Nk=1 << 16, Hq=1 << 15, Hkv=1 << 15), E.ATTN_ERR_UNSUPPORTED),  # rows >= 2^31
-    (dict(B=0), E.ATTN_OK),
-    (dict(Nq=0, Nk=0, q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk=None, dv=None, ws=None),
-     E.ATTN_OK),
+    (dict(B=0), E.ATTN_ERR_INVALID_ARG),                # every size >= 1
+    (dict(Nq=0), E.ATTN_ERR_INVALID_ARG),
+    (dict(Nk=0), E.ATTN_ERR_INVALID_ARG),
 ])
 def test_bwd_validation(kw, status):
     assert bwd(**kw) == status
@@ -201,6 +269,7 @@ def test_bwd_workspace_bytes():
     assert E.attn_bwd_workspace_bytes(2, 8, 100) == 2 * 8 * 100 * 8
     assert E.attn_bwd_workspace_bytes(0, 8, 100) == 0
     assert E.attn_bwd_workspace_bytes(1, 0, 100) == 0
+    assert E.attn_bwd_workspace_bytes(1, 4, 0) == 0
     assert E.attn_bwd_workspace_bytes(1, 4, -1) == 0
 
 
@@ -219,8 +288,9 @@ def fwd8(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=128, scale=0
     (dict(v=None), E.ATTN_ERR_INVALID_ARG),
     (dict(k=P + 8), E.ATTN_ERR_INVALID_ARG),
     (dict(lse=P + 1), E.ATTN_ERR_INVALID_ARG),
-    (dict(B=0), E.ATTN_OK),
-    (dict(Nq=0), E.ATTN_OK),
+    (dict(B=0), E.ATTN_ERR_INVALID_ARG),                # every size >= 1
+    (dict(Nq=0), E.ATTN_ERR_INVALID_ARG),
+    (dict(Nk=0), E.ATTN_ERR_INVALID_ARG),
 ])
 def test_fwd_fp8_validation(kw, status):
     assert fwd8(**kw) == status

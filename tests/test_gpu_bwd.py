@@ -105,26 +105,16 @@ def test_bwd_scales(orc, scale):
         check_grad("dv", dv, rv)
 
 
-def test_bwd_empty_sides():
-    """Nq = 0 gives dk = dv = 0; Nk = 0 gives dq = 0."""
-    q, k, v, do = I.bwd_inputs(1, 2, 1, 0, 70, 128, "bf16", seed=5)
-    say("[bwd] Nq = 0")
-    qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
-    o = torch.empty_like(qd)
-    lse = torch.empty(1, 2, 0, dtype=torch.float32, device="cuda")
-    dk = torch.full_like(kd, float("nan"))
-    dv = torch.full_like(vd, float("nan"))
-    E.attn_bwd(qd, kd, vd, o, dod, lse, dk=dk, dv=dv)
-    torch.cuda.synchronize()
-    assert (dk == 0).all().item() and (dv == 0).all().item()
-    q, k, v, do = I.bwd_inputs(1, 2, 1, 40, 0, 64, "bf16", seed=6)
-    say("[bwd] Nk = 0")
-    qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
-    o, lse = E.attn_fwd(qd, kd, vd, causal=False)
-    dq = torch.full_like(qd, float("nan"))
-    E.attn_bwd(qd, kd, vd, o, dod, lse, dq=dq)
-    torch.cuda.synchronize()
-    assert (dq == 0).all().item()
+def test_bwd_empty_sides_rejected():
+    """Nq = 0 or Nk = 0 is an invalid size: refused before any launch."""
+    for Nq, Nk in ((0, 70), (40, 0)):
+        q, k, v, do = I.bwd_inputs(1, 2, 1, Nq, Nk, 128, "bf16", seed=5)
+        say("[bwd] Nq = %d, Nk = %d" % (Nq, Nk))
+        qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
+        lse = torch.zeros(1, 2, Nq, dtype=torch.float32, device="cuda")
+        with pytest.raises(E.AttnError) as ei:
+            E.attn_bwd(qd, kd, vd, torch.zeros_like(qd), dod, lse)
+        assert ei.value.status == E.ATTN_ERR_INVALID_ARG
 
 
 def test_bwd_deterministic():

@@ -81,13 +81,21 @@ def test_many_short_sequences(orc, kps):
     assert (o[sl.numpy() == 0] == 0).all() and np.isneginf(lse[sl.numpy() == 0]).all()
 
 
-def test_empty_cache():
-    """max_seq_len = 0: every row sees no key."""
+def test_empty_cache_rejected():
+    """max_seq_len = 0 (and B = 0) are invalid sizes: the call is refused
+    before any launch and leaves o untouched."""
     B, Hq, Hkv, d = 3, 8, 2, 64
-    q = torch.randn(B, Hq, d).to(torch.bfloat16)
-    kc = torch.empty(B, Hkv, 0, d, dtype=torch.bfloat16)
-    o, lse = gpu_decode(torch.zeros(B, dtype=torch.int32), q, kc, kc.clone(), 0.125)
-    assert (o == 0).all() and np.isneginf(lse).all()
+    q = dev(torch.randn(B, Hq, d).to(torch.bfloat16))
+    kc = torch.empty(B, Hkv, 0, d, dtype=torch.bfloat16, device="cuda")
+    o = torch.full_like(q, 7.0)
+    with pytest.raises(E.AttnError) as ei:
+        E.attn_decode(q, kc, kc.clone(), dev(torch.zeros(B, dtype=torch.int32)), o=o)
+    assert ei.value.status == E.ATTN_ERR_INVALID_ARG
+    with pytest.raises(E.AttnError) as ei:
+        E.attn_decode(q[:0], kc[:0], kc[:0], dev(torch.zeros(0, dtype=torch.int32)))
+    assert ei.value.status == E.ATTN_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert (o == 7.0).all().item()
 
 
 def test_nan_padding_never_read():
@@ -225,9 +233,11 @@ def test_paged_shared_prefix_unused_blocks_and_clamping(orc):
     _paged_parity(orc, sl, q, kp, vp, bt2, 0.088, "clamped entries")
 
 
-def test_paged_empty_pool():
-    q = torch.randn(3, 8, 64).to(torch.bfloat16)
-    kp = torch.empty(0, 2, 32, 64, dtype=torch.bfloat16)
-    bt = torch.zeros(3, 4, dtype=torch.int32)
-    o, lse = gpu_decode_paged(torch.tensor([5, 0, 100], dtype=torch.int32), q, kp, kp.clone(), bt, 0.125)
-    assert (o == 0).all() and np.isneginf(lse).all()
+def test_paged_empty_pool_rejected():
+    """A pool of no blocks is an invalid size: refused before any launch."""
+    q = dev(torch.randn(3, 8, 64).to(torch.bfloat16))
+    kp = torch.empty(0, 2, 32, 64, dtype=torch.bfloat16, device="cuda")
+    bt = dev(torch.zeros(3, 4, dtype=torch.int32))
+    with pytest.raises(E.AttnError) as ei:
+        E.attn_decode_paged(q, kp, kp.clone(), bt, dev(torch.tensor([5, 0, 100], dtype=torch.int32)))
+    assert ei.value.status == E.ATTN_ERR_INVALID_ARG

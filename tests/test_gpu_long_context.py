@@ -5,15 +5,18 @@ workgroup falls inside the same few segments and the merge kernel folds about
 a hundred partial results per segment; a second batch mixes that length with
 a 3-key sequence and an empty one.  Prefill: a short ragged query chunk
 attending to 65536 keys, causal with bottom-right alignment and non-causal,
-compared on sampled rows (every head's first and last rows, tile edges and
-random rows)."""
+compared on every output element.  Each case also bounds the error relative
+to the largest output of each sequence (decode) or head (prefill): over this
+many keys the outputs shrink to a few hundredths, where the absolute bf16
+bound alone would not constrain them."""
 import numpy as np
 import pytest
 import torch
 
 import exact_scaled_dot_sdpa_amd as E
 from exact_scaled_dot_sdpa_amd import inputs as I
-from gpu_util import TOL_LSE, TOL_O, assert_close, dev, gpu_decode, sample_rows, say
+from gpu_util import TOL_LSE, TOL_O, assert_close, assert_rel_per_group, dev, gpu_decode, say
+from gpu_util import gpu_fwd as gpu_fwd_np
 
 pytestmark = pytest.mark.gpu
 
@@ -27,6 +30,7 @@ def test_decode_one_long_sequence(orc):
     o, lse = gpu_decode(sl, q, kc, vc, 128 ** -0.5)
     o_ref, lse_ref = orc.decode(I.to_f64(q), I.to_f64(kc), I.to_f64(vc), sl.numpy(), 128 ** -0.5)
     assert_close("L=2^17 O", o, o_ref, TOL_O["bf16"])
+    assert_rel_per_group("L=2^17 O", o, o_ref, 1)
     assert_close("L=2^17 LSE", lse, lse_ref, TOL_LSE)
 
 
@@ -37,6 +41,7 @@ def test_decode_long_mixed_with_short_and_empty(orc):
     o, lse = gpu_decode(sl, q, kc, vc, 0.125)
     o_ref, lse_ref = orc.decode(I.to_f64(q), I.to_f64(kc), I.to_f64(vc), sl.numpy(), 0.125)
     assert_close("mixed O", o, o_ref, TOL_O["bf16"])
+    assert_rel_per_group("mixed O (sequences 0, 1)", o[:2], o_ref[:2], 1)
     assert_close("mixed LSE", lse, lse_ref, TOL_LSE)
     assert (o[2] == 0).all() and np.isneginf(lse[2]).all(), "empty sequence: O = 0 and LSE = -inf"
 
@@ -46,15 +51,11 @@ def test_prefill_short_chunk_over_long_keys(orc, causal):
     B, Hq, Hkv, Nq, Nk, d = 1, 8, 2, 300, 1 << 16, 128
     q, k, v = I.prefill_inputs(B, Hq, Hkv, Nq, Nk, d, "bf16", seed=903 + causal)
     say("[prefill-long] q%s k%s causal=%s" % (tuple(q.shape), tuple(k.shape), causal))
-    o, lse = E.attn_fwd(dev(q), dev(k), dev(v), scale=d ** -0.5, causal=causal)
-    torch.cuda.synchronize()
-    rows = sample_rows(B, Hq, Nq, 96, seed=904)
-    o_ref, lse_ref = orc.attn_rows(I.to_f64(q), I.to_f64(k), I.to_f64(v), d ** -0.5, causal, rows)
-    og = o[rows[:, 0], rows[:, 1], rows[:, 2]]
-    lg = lse[rows[:, 0], rows[:, 1], rows[:, 2]]
-    assert_close("Nk=2^16 O (%d rows)" % len(rows), I.to_f64(og), o_ref, TOL_O["bf16"])
-    assert_close("Nk=2^16 LSE", I.to_f64(lg), lse_ref, TOL_LSE)
-    assert torch.isfinite(o.float()).all().item(), "non-finite output somewhere in the full tensor"
+    o, lse = gpu_fwd_np(q, k, v, d ** -0.5, causal)
+    o_ref, lse_ref = orc.attn(I.to_f64(q), I.to_f64(k), I.to_f64(v), d ** -0.5, causal)
+    assert_close("Nk=2^16 O", o, o_ref, TOL_O["bf16"])
+    assert_rel_per_group("Nk=2^16 O", o, o_ref, 2)
+    assert_close("Nk=2^16 LSE", lse, lse_ref, TOL_LSE)
 
 
 def test_paged_decode_long_sequences(orc):
@@ -69,4 +70,5 @@ def test_paged_decode_long_sequences(orc):
     torch.cuda.synchronize()
     o_ref, lse_ref = orc.decode_paged(I.to_f64(q), I.to_f64(kp), I.to_f64(vp), bt.numpy(), sl.numpy(), 128 ** -0.5)
     assert_close("paged L>=1e5 O", I.to_f64(o), o_ref, TOL_O["bf16"])
+    assert_rel_per_group("paged L>=1e5 O", I.to_f64(o), o_ref, 1)
     assert_close("paged L>=1e5 LSE", I.to_f64(lse), lse_ref, TOL_LSE)

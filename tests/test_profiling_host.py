@@ -40,7 +40,7 @@ def test_stats_last_dispatches(tmp_path):
     out = tmp_path / "s.md"
     text = P.stats(str(st), "cmd", str(out), str(tr), last=2)
     assert "| prefill_bf16_kernel | 4 | 1500.00 | 1000.00 | 3000.00 | 99.50% |" in text
-    assert "| prefill_bf16_kernel | 2 | 1100.00 |" in text
+    assert "| prefill_bf16_kernel | 2 | 1100.00 | 1100.00 |" in text
 
 
 def test_traffic_scaling(tmp_path, monkeypatch):
@@ -85,8 +85,14 @@ def test_counters_derived_figures(tmp_path):
             rows.append([name, 1, 0, dur, c, v])
     path = tmp_path / "pmc.csv"
     _write(path, hdr, rows)
+    js = tmp_path / "c.json"
     text = P.counters(str(path), "cmd", str(tmp_path / "c.md"),
-                      {"prefill_bf16_kernel": 1.0e12, "prefill_fp8_kernel": 1.0e12})
+                      {"prefill_bf16_kernel": 1.0e12, "prefill_fp8_kernel": 1.0e12}, str(js))
+    doc = json.load(open(js))
+    assert doc["kernels"]["prefill"]["clock_ghz"] == pytest.approx(1.6)
+    assert doc["kernels"]["prefill"]["mfma_busy"] == pytest.approx(0.5)
+    assert doc["kernels"]["fp8"]["clock_ghz"] == pytest.approx(1.6)
+    assert "decode" not in doc["kernels"]  # absent from the run: no entry
     line = [l for l in text.splitlines() if l.startswith("| prefill_bf16_kernel | 1000.0 |")][0]
     cells = [c.strip() for c in line.strip("|").split("|")]
     assert cells[2] == "1.60"        # clock
