@@ -31,7 +31,14 @@ def lib():
         raise RuntimeError(
             "libattn.so is not built (expected at %s); run `python -m exact_scaled_dot_sdpa_amd.build`"
             % _LIB_PATH)
-    L = ctypes.CDLL(_LIB_PATH)
+    L = bind_signatures(ctypes.CDLL(_LIB_PATH))
+    _lib = L
+    return L
+
+
+def bind_signatures(L):
+    """Set the argument and result types of every entry point of include/attn.h
+    on the ctypes library L; returns L."""
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
     L.attn_fwd.restype = i
@@ -53,7 +60,6 @@ def lib():
     L.attn_bwd.restype = i
     L.attn_status_str.argtypes = [i]
     L.attn_status_str.restype = ctypes.c_char_p
-    _lib = L
     return L
 
 

@@ -1,0 +1,19 @@
+// Launch stubs for a host-only build of the C-ABI layer (attn_api.hip): every
+// kernel launcher returns success without touching a device, so that argument
+// validation, workspace sizing and dispatch can run under the address and
+// undefined-behaviour sanitizers on a machine without a GPU.  Test code only.
+#include "kernels.h"
+
+namespace attn {
+
+hipError_t launch_prefill_bf16(const FwdArgs &, hipStream_t) { return hipSuccess; }
+hipError_t launch_prefill_f32(const FwdArgs &, hipStream_t) { return hipSuccess; }
+hipError_t launch_prefill_fp8(const Fp8FwdArgs &, hipStream_t) { return hipSuccess; }
+hipError_t launch_decode_bf16(const DecodeArgs &, hipStream_t) { return hipSuccess; }
+hipError_t launch_bwd_bf16(const BwdArgs &, hipStream_t) { return hipSuccess; }
+hipError_t device_cu_count(int *out) {
+    *out = 256;
+    return hipSuccess;
+}
+
+}  // namespace attn

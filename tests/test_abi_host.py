@@ -83,11 +83,11 @@ def test_status_strings():
     assert E.attn_status_str(99) == "ATTN_ERR_UNKNOWN"
 
 
-def fwd(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64, scale=0.125, causal=0, dtype=1):
-    return E.lib().attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, None)
+def fwd(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64, scale=0.125, causal=0, dtype=1, L=None):
+    return (L or E.lib()).attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, None)
 
 
-@pytest.mark.parametrize("kw,status", [
+FWD_CASES = [
     (dict(Hq=3, Hkv=2), E.ATTN_ERR_INVALID_ARG),        # Hq % Hkv != 0
     (dict(Hq=0), E.ATTN_ERR_INVALID_ARG),
     (dict(Hkv=0), E.ATTN_ERR_INVALID_ARG),
@@ -111,21 +111,25 @@ def fwd(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=64, scale=0.1
     (dict(Nk=0), E.ATTN_ERR_INVALID_ARG),
     (dict(Nq=0, Nk=0, causal=1), E.ATTN_ERR_INVALID_ARG),
     (dict(Nq=1 << 16, Hq=1 << 15, Hkv=1 << 15), E.ATTN_ERR_UNSUPPORTED),  # rows >= 2^31
-])
+]
+
+
+@pytest.mark.parametrize("kw,status", FWD_CASES)
 def test_fwd_validation(kw, status):
     assert fwd(**kw) == status
 
 
 def dec(q=P, kc=P, vc=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Lmax=512, d=128, scale=0.09, kps=None, dtype=1,
-        ws=P, ws_bytes=1 << 30):
+        ws=P, ws_bytes=1 << 30, L=None):
     """attn_decode, or attn_decode_split when kps is given."""
+    L = L or E.lib()
     if kps is None:
-        return E.lib().attn_decode(q, kc, vc, sl, o, lse, B, Hq, Hkv, Lmax, d, scale, dtype, ws, ws_bytes, None)
-    return E.lib().attn_decode_split(q, kc, vc, sl, o, lse, B, Hq, Hkv, Lmax, d, scale, kps, dtype, ws, ws_bytes,
+        return L.attn_decode(q, kc, vc, sl, o, lse, B, Hq, Hkv, Lmax, d, scale, dtype, ws, ws_bytes, None)
+    return L.attn_decode_split(q, kc, vc, sl, o, lse, B, Hq, Hkv, Lmax, d, scale, kps, dtype, ws, ws_bytes,
                                      None)
 
 
-@pytest.mark.parametrize("kw,status", [
+DEC_CASES = [
     (dict(Hq=6, Hkv=4), E.ATTN_ERR_INVALID_ARG),
     (dict(B=-1), E.ATTN_ERR_INVALID_ARG),
     (dict(Lmax=-1), E.ATTN_ERR_INVALID_ARG),
@@ -147,7 +151,10 @@ def dec(q=P, kc=P, vc=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Lmax=512, d=128, sc
     (dict(kps=100, B=0), E.ATTN_ERR_INVALID_ARG),
     (dict(kps=100, ws_bytes=1024), E.ATTN_ERR_WORKSPACE),
     (dict(B=1 << 16, Hkv=1 << 4, Hq=1 << 4, Lmax=1 << 12), E.ATTN_ERR_UNSUPPORTED),  # cache rows >= 2^31
-])
+]
+
+
+@pytest.mark.parametrize("kw,status", DEC_CASES)
 def test_decode_validation(kw, status):
     assert dec(**kw) == status
 
@@ -190,12 +197,12 @@ def test_decode_workspace_bytes():
 
 
 def pdec(q=P, kp=P, vp=P, bt=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, nb=16, bs=32, mb=8, d=128, scale=0.09, kps=0,
-         dtype=1, ws=P, ws_bytes=1 << 30):
-    return E.lib().attn_decode_paged(q, kp, vp, bt, sl, o, lse, B, Hq, Hkv, nb, bs, mb, d, scale, kps, dtype, ws,
+         dtype=1, ws=P, ws_bytes=1 << 30, L=None):
+    return (L or E.lib()).attn_decode_paged(q, kp, vp, bt, sl, o, lse, B, Hq, Hkv, nb, bs, mb, d, scale, kps, dtype, ws,
                                      ws_bytes, None)
 
 
-@pytest.mark.parametrize("kw,status", [
+PDEC_CASES = [
     (dict(nb=-1), E.ATTN_ERR_INVALID_ARG),
     (dict(bs=0), E.ATTN_ERR_INVALID_ARG),
     (dict(mb=-1), E.ATTN_ERR_INVALID_ARG),
@@ -214,7 +221,10 @@ def pdec(q=P, kp=P, vp=P, bt=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, nb=16, bs=32
     (dict(mb=0), E.ATTN_ERR_INVALID_ARG),
     (dict(kps=-1), E.ATTN_ERR_INVALID_ARG),
     (dict(B=100, mb=1 << 16, bs=1 << 10, nb=4), E.ATTN_ERR_UNSUPPORTED),  # 64 sequences' keys >= 2^31
-])
+]
+
+
+@pytest.mark.parametrize("kw,status", PDEC_CASES)
 def test_decode_paged_validation(kw, status):
     assert pdec(**kw) == status
 
@@ -230,12 +240,12 @@ def test_decode_paged_workspace_is_the_contiguous_one():
 
 
 def bwd(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, Hq=4, Hkv=2, Nq=64, Nk=64, d=128, scale=0.09,
-        causal=0, dtype=1, ws=P, ws_bytes=1 << 30):
-    return E.lib().attn_bwd(q, k, v, o, do, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, ws,
+        causal=0, dtype=1, ws=P, ws_bytes=1 << 30, L=None):
+    return (L or E.lib()).attn_bwd(q, k, v, o, do, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, ws,
                             ws_bytes, None)
 
 
-@pytest.mark.parametrize("kw,status", [
+BWD_CASES = [
     (dict(Hq=3, Hkv=2), E.ATTN_ERR_INVALID_ARG),
     (dict(Hkv=0), E.ATTN_ERR_INVALID_ARG),
     (dict(B=-1), E.ATTN_ERR_INVALID_ARG),
@@ -260,7 +270,10 @@ def bwd(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, Hq=4, Hkv=2, Nq=
     (dict(B=0), E.ATTN_ERR_INVALID_ARG),                # every size >= 1
     (dict(Nq=0), E.ATTN_ERR_INVALID_ARG),
     (dict(Nk=0), E.ATTN_ERR_INVALID_ARG),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status", BWD_CASES)
 def test_bwd_validation(kw, status):
     assert bwd(**kw) == status
 
@@ -273,11 +286,12 @@ def test_bwd_workspace_bytes():
     assert E.attn_bwd_workspace_bytes(1, 4, -1) == 0
 
 
-def fwd8(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=128, scale=0.09, v_scale=1.0, causal=0):
-    return E.lib().attn_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, v_scale, causal, None)
+def fwd8(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=128, scale=0.09, v_scale=1.0, causal=0,
+         L=None):
+    return (L or E.lib()).attn_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, v_scale, causal, None)
 
 
-@pytest.mark.parametrize("kw,status", [
+FWD8_CASES = [
     (dict(Hq=3, Hkv=2), E.ATTN_ERR_INVALID_ARG),
     (dict(Nk=-1), E.ATTN_ERR_INVALID_ARG),
     (dict(causal=1, Nq=9), E.ATTN_ERR_INVALID_ARG),
@@ -291,6 +305,15 @@ def fwd8(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nk=8, d=128, scale=0
     (dict(B=0), E.ATTN_ERR_INVALID_ARG),                # every size >= 1
     (dict(Nq=0), E.ATTN_ERR_INVALID_ARG),
     (dict(Nk=0), E.ATTN_ERR_INVALID_ARG),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status", FWD8_CASES)
 def test_fwd_fp8_validation(kw, status):
     assert fwd8(**kw) == status
+
+
+# Every case table with the call it feeds: (helper, cases).  A run of the same
+# tables against a host-only build of the validation layer (kernel launches
+# stubbed) under address and undefined-behaviour sanitizers uses this list.
+ALL_TABLES = [(fwd, FWD_CASES), (dec, DEC_CASES), (pdec, PDEC_CASES), (bwd, BWD_CASES), (fwd8, FWD8_CASES)]
