@@ -13,6 +13,7 @@ Functions carry the names of the C entry points:
                 workspace=None, return_lse=True)
     attn_decode_split(q, k_cache, v_cache, seq_lens, keys_per_split, scale=None, o=None,
                       lse=None, workspace=None, return_lse=True)
+    attn_decode_noalloc(q, k_cache, v_cache, seq_lens, o, lse=None, scale=None)
     attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, o=None,
                       lse=None, workspace=None, keys_per_split=0, return_lse=True)
     attn_decode_workspace_bytes(B, Hq, Hkv, max_seq_len, d)
@@ -37,6 +38,7 @@ from ._binding import (  # noqa: F401
     attn_bwd,
     attn_bwd_workspace_bytes,
     attn_decode,
+    attn_decode_noalloc,
     attn_decode_paged,
     attn_decode_split,
     attn_decode_split_workspace_bytes,
@@ -52,6 +54,7 @@ __all__ = [
     "attn_fwd",
     "attn_fwd_fp8",
     "attn_decode",
+    "attn_decode_noalloc",
     "attn_decode_paged",
     "attn_decode_split",
     "attn_decode_workspace_bytes",

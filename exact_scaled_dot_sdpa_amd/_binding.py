@@ -50,6 +50,8 @@ def bind_signatures(L):
     L.attn_decode.restype = i
     L.attn_decode_split.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
     L.attn_decode_split.restype = i
+    L.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    L.attn_decode_noalloc.restype = i
     L.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp, sz, vp]
     L.attn_decode_paged.restype = i
     L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, i, vp]
@@ -274,6 +276,29 @@ def attn_decode(q, k_cache, v_cache, seq_lens, scale=None, o=None, lse=None, wor
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode")
     return (o, lse) if return_lse else o
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, seq_lens, o, lse=None, scale=None, stream=None):
+    """attn_decode with no workspace: the partial results go to the library's
+    own device array (ATTN_DECODE_NOALLOC_MAX_BYTES), so the call allocates
+    nothing.  o [B,Hq,d] and lse [B,Hq] (or None) are the caller's.  Calls
+    that overlap in time on one device share that array and race."""
+    B, Hq, Hkv, Lmax, d = _decode_shapes(q, k_cache, v_cache, seq_lens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check_dev("o", o, q.dtype)
+    if tuple(o.shape) != tuple(q.shape):
+        raise ValueError("o must have q's shape %s, got %s" % (tuple(q.shape), tuple(o.shape)))
+    if lse is not None:
+        _check_dev("lse", lse, _torch().float32)
+        if tuple(lse.shape) != (B, Hq):
+            raise ValueError("lse must be [B,Hq] = %s, got %s" % ((B, Hq), tuple(lse.shape)))
+    st = lib().attn_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+                                   o.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                   B, Hq, Hkv, Lmax, d, float(scale), _dtype_code(q), _stream_handle(q, stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_noalloc")
+    return o, lse
 
 
 def attn_decode_split(q, k_cache, v_cache, seq_lens, keys_per_split, scale=None, o=None, lse=None, workspace=None,

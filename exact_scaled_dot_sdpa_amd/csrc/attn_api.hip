@@ -8,6 +8,9 @@
 
 #include "kernels.h"
 
+static_assert(attn::DECODE_SCRATCH_BYTES == ATTN_DECODE_NOALLOC_MAX_BYTES,
+              "the header states the scratch array's size");
+
 namespace {
 
 // Upper bound on the workgroups of the decode split kernel; the default
@@ -154,12 +157,14 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_seq_len, int 
 
 namespace {
 
-// Shared body of attn_decode and attn_decode_paged; the paged cache passes
-// block_table != nullptr and Lmax = max_blocks * block_size.
+// Shared body of the decode entry points; the paged cache passes
+// block_table != nullptr and Lmax = max_blocks * block_size.  use_scratch:
+// the partial results go to the library's device scratch array (workspace
+// arguments ignored), after every check and only if they fit in it.
 int decode_call(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens, void *o, float *lse,
                 int B, int Hq, int Hkv, int Lmax, int d, float scale, int keys_per_split, attn_dtype_t dtype,
                 void *workspace, size_t workspace_bytes, hipStream_t stream, const int32_t *block_table,
-                int block_size, int max_blocks, int num_blocks)
+                int block_size, int max_blocks, int num_blocks, bool use_scratch = false)
 {
     if (!decode_sizes_ok(B, Hq, Hkv, Lmax)) return ATTN_ERR_INVALID_ARG;
     if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
@@ -181,6 +186,11 @@ int decode_call(const void *q, const void *k_cache, const void *v_cache, const i
         return ATTN_ERR_UNSUPPORTED;
     size_t ob, need;
     workspace_layout(p, d, &ob, &need);
+    if (use_scratch) {
+        if (need > attn::DECODE_SCRATCH_BYTES) return ATTN_ERR_WORKSPACE;
+        if (attn::decode_scratch(&workspace) != hipSuccess) return ATTN_ERR_LAUNCH;
+        workspace_bytes = attn::DECODE_SCRATCH_BYTES;
+    }
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return ATTN_ERR_WORKSPACE;
 
     attn::DecodeArgs a{q, k_cache, v_cache, seq_lens, o, lse, B, Hq, Hkv, Lmax, d, scale,
@@ -200,6 +210,14 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, const i
 {
     return decode_call(q, k_cache, v_cache, seq_lens, o, lse, B, Hq, Hkv, max_seq_len, d, scale, 0, dtype,
                        workspace, workspace_bytes, stream, nullptr, 0, 0, 0);
+}
+
+int attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens, void *o,
+                        float *lse, int B, int Hq, int Hkv, int max_seq_len, int d, float scale, attn_dtype_t dtype,
+                        hipStream_t stream)
+{
+    return decode_call(q, k_cache, v_cache, seq_lens, o, lse, B, Hq, Hkv, max_seq_len, d, scale, 0, dtype, nullptr,
+                       0, stream, nullptr, 0, 0, 0, true);
 }
 
 int attn_decode_split(const void *q, const void *k_cache, const void *v_cache, const int32_t *seq_lens, void *o,

@@ -63,4 +63,12 @@ hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream);
 // Compute units of the current device (queried once per device, cached).
 hipError_t device_cu_count(int *out);
 
+// Size of the decode kernels' file-scope device scratch array, which serves
+// callers that cannot allocate (attn_decode_noalloc).
+constexpr size_t DECODE_SCRATCH_BYTES = size_t(32) << 20;
+
+// Device address of that array on the current device (looked up once per
+// device with hipGetSymbolAddress and kept).
+hipError_t decode_scratch(void **out);
+
 }  // namespace attn

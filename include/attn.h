@@ -243,6 +243,28 @@ int attn_decode_split(const void *q, const void *k_cache, const void *v_cache,
                       size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * attn_decode_noalloc -- attn_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Arguments, result and errors are attn_decode's, with no
+ * workspace: the split's partial results go to a device array inside the
+ * library, ATTN_DECODE_NOALLOC_MAX_BYTES (32 MiB) on each device the library
+ * runs on, held until the process ends.  Sizes whose
+ * attn_decode_workspace_bytes(B, Hq, Hkv, max_seq_len, d) exceeds it return
+ * ATTN_ERR_WORKSPACE (nothing launched).  The call allocates nothing; its
+ * first call on a device looks the array's address up (hipGetSymbolAddress)
+ * and keeps it.  Every call on one device shares that array: two calls that
+ * overlap in time on one device (different streams or threads) race and give
+ * undefined results; calls ordered on one stream are safe.  Nothing in the
+ * array needs to start at zero.
+ */
+#define ATTN_DECODE_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+int attn_decode_noalloc(const void *q, const void *k_cache,
+                        const void *v_cache, const int32_t *seq_lens, void *o,
+                        float *lse, int B, int Hq, int Hkv, int max_seq_len,
+                        int d, float scale, attn_dtype_t dtype,
+                        hipStream_t stream);
+
+/*
  * attn_decode_paged -- attn_decode against a paged KV cache: each sequence's
  * cached rows live in fixed-size blocks anywhere in a pool, found through a
  * block table ("Transformer 笔记：注意力机制为什么会变成系统问题", the

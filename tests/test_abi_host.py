@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert names == sorted(["attn_fwd", "attn_decode", "attn_decode_paged", "attn_decode_workspace_bytes",
-                            "attn_decode_split", "attn_decode_split_workspace_bytes",
+                            "attn_decode_split", "attn_decode_split_workspace_bytes", "attn_decode_noalloc",
                             "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_fp8", "attn_status_str"])
     lib = ctypes.CDLL(E.lib_path())
     for n in names:
@@ -313,7 +313,47 @@ def test_fwd_fp8_validation(kw, status):
     assert fwd8(**kw) == status
 
 
+def dec0(q=P, kc=P, vc=P, sl=P, o=P, lse=P, B=2, Hq=8, Hkv=2, Lmax=512, d=128, scale=0.09, dtype=1, L=None):
+    return (L or E.lib()).attn_decode_noalloc(q, kc, vc, sl, o, lse, B, Hq, Hkv, Lmax, d, scale, dtype, None)
+
+
+NOALLOC_CASES = [
+    (dict(Hq=6, Hkv=4), E.ATTN_ERR_INVALID_ARG),
+    (dict(B=0), E.ATTN_ERR_INVALID_ARG),
+    (dict(Lmax=0), E.ATTN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), E.ATTN_ERR_INVALID_ARG),
+    (dict(dtype=0), E.ATTN_ERR_UNSUPPORTED),
+    (dict(d=96), E.ATTN_ERR_UNSUPPORTED),
+    (dict(sl=None), E.ATTN_ERR_INVALID_ARG),
+    (dict(o=P + 2), E.ATTN_ERR_INVALID_ARG),
+    (dict(kc=None), E.ATTN_ERR_INVALID_ARG),
+    # partial results beyond the library's 32 MiB array: refused before any HIP call
+    (dict(B=2000, Hq=128, Hkv=8, Lmax=1), E.ATTN_ERR_WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("kw,status", NOALLOC_CASES)
+def test_decode_noalloc_validation(kw, status):
+    assert dec0(**kw) == status
+
+
+def test_decode_noalloc_limit_is_the_headers():
+    """The refusal threshold is the workspace attn_decode would need against
+    ATTN_DECODE_NOALLOC_MAX_BYTES (32 MiB): the largest batch that fits is
+    not refused for size (on a machine without a GPU the call then fails at
+    the device lookup, after validation), one more sequence is."""
+    text = open(HEADER).read()
+    assert re.search(r"#define ATTN_DECODE_NOALLOC_MAX_BYTES \(\(size_t\)32 << 20\)", text)
+    cap = 32 << 20
+    B = 1
+    while E.attn_decode_workspace_bytes(B + 1, 32, 8, 64, 128) <= cap:
+        B += 1
+    assert dec0(B=B + 1, Hq=32, Hkv=8, Lmax=64) == E.ATTN_ERR_WORKSPACE
+    assert dec0(B=B, Hq=32, Hkv=8, Lmax=64) != E.ATTN_ERR_WORKSPACE
+
+
 # Every case table with the call it feeds: (helper, cases).  A run of the same
 # tables against a host-only build of the validation layer (kernel launches
 # stubbed) under address and undefined-behaviour sanitizers uses this list.
-ALL_TABLES = [(fwd, FWD_CASES), (dec, DEC_CASES), (pdec, PDEC_CASES), (bwd, BWD_CASES), (fwd8, FWD8_CASES)]
+ALL_TABLES = [(fwd, FWD_CASES), (dec, DEC_CASES), (pdec, PDEC_CASES), (bwd, BWD_CASES), (fwd8, FWD8_CASES),
+              (dec0, NOALLOC_CASES)]
