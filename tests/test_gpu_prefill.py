@@ -63,6 +63,11 @@ RAGGED = [
     ("f32", 64, 2, 2, 1, 100, 100, True),
     ("f32", 128, 1, 4, 2, 70, 130, True),
     ("f32", 128, 1, 2, 1, 33, 17, False),
+    # grids of at least 256 row tiles of 16: the four-rows-per-wave fp32 form
+    ("f32", 64, 2, 8, 4, 250, 250, True),
+    ("f32", 128, 1, 16, 2, 260, 300, True),    # chunked prefill
+    ("f32", 128, 1, 16, 16, 256, 100, False),  # Nk < Nq, one partial key tile
+    ("f32", 64, 1, 16, 4, 300, 200, False),    # Nq > Nk, ragged row and key tails
 ]
 
 
