@@ -24,6 +24,15 @@
 //         stays as finely balanced as with 32-row tiles.
 //     The wide forms are used when the grid still holds two workgroups per
 //     CU.  Each row's arithmetic is the same in every form.
+//   * Key split, for causal grids of fewer 128-row workgroups than CUs (one
+//     short layer): there the rows nearest the end of K set the time, since a
+//     wave walks every visible key of its rows.  An 8-wave workgroup then
+//     holds SK key groups of NW / SK waves over the same rows (4 x 2 waves
+//     and 64 rows for d = 64, 2 x 4 waves and 128 rows for d = 128); group g
+//     walks the g-th of SK equal runs of the row tile's key tiles through its
+//     own LDS buffers, and at the end the groups' (O^T, reference, l) are
+//     merged through LDS by one more step of the online-softmax recurrence.
+//     Only the order of the sums differs from the other forms.
 //   * K and V tiles go from HBM straight into LDS with global_load_lds_dwordx4
 //     (no staging registers, no VALU work), double-buffered so the next tile
 //     lands while the current one is computed; one barrier per tile.  Both
@@ -121,19 +130,21 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-template <int D, bool CAUSAL, int NW, int HP>
+template <int D, bool CAUSAL, int NW, int HP, int SK>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
     __bf16 *__restrict__ O, float *__restrict__ LSE, int Hq, int Hkv, int Nq, int Nk,
     float sl2, int n_qtiles, int total)
 {
-    using C = Cfg<D, NW>;
-    constexpr int BMP = 32 * (NW / HP);  // query positions per workgroup
-    // double-buffered K and V tiles, row-major, chunk-swizzled
-    __shared__ __attribute__((aligned(1024))) __bf16 sK0[C::TILE];
-    __shared__ __attribute__((aligned(1024))) __bf16 sK1[C::TILE];
-    __shared__ __attribute__((aligned(1024))) __bf16 sV0[C::TILE];
-    __shared__ __attribute__((aligned(1024))) __bf16 sV1[C::TILE];
+    constexpr int NWG = NW / SK;          // waves per key group
+    using C = Cfg<D, NWG>;
+    constexpr int BMP = 32 * (NWG / HP);  // query positions per workgroup
+    // double-buffered K and V tiles, row-major, chunk-swizzled; key group g
+    // uses elements [g TILE, (g + 1) TILE) of each
+    __shared__ __attribute__((aligned(1024))) __bf16 sK0[SK * C::TILE];
+    __shared__ __attribute__((aligned(1024))) __bf16 sK1[SK * C::TILE];
+    __shared__ __attribute__((aligned(1024))) __bf16 sV0[SK * C::TILE];
+    __shared__ __attribute__((aligned(1024))) __bf16 sV1[SK * C::TILE];
 
     // ---- work item: XCD-contiguous remap of the linear block id ----------
     const int L = blockIdx.x;
@@ -153,7 +164,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int wave_all = __builtin_amdgcn_readfirstlane(wave);
+    const int grp = SK > 1 ? wave_all / NWG : 0;       // key group
+    const int wave_u = SK > 1 ? wave_all % NWG : wave_all;  // wave within the group
     const int h = hk * G + gqb * HP + wave_u % HP;  // this wave's query head
     const int prow = q0 + (wave_u / HP) * 32;       // this wave's first query row
     const int n = lane & 31, g = lane >> 5;
@@ -197,6 +210,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(
         kv_end = e < Nk ? e : Nk;
     }
     const int ntiles = (kv_end + BN - 1) / BN;
+    // key group grp walks tiles [tb, tb + cnt); all groups step through nit
+    // iterations together (a group with fewer tiles idles in the last one)
+    int tb = 0, cnt = ntiles, nit = ntiles;
+    if constexpr (SK > 1) {
+        tb = ntiles * grp / SK;
+        cnt = ntiles * (grp + 1) / SK - tb;
+        nit = (ntiles + SK - 1) / SK;
+    }
 
     // per-lane limit of visible keys (inclusive)
     const int lim = CAUSAL ? ((qi + off) < (Nk - 1) ? (qi + off) : (Nk - 1)) : (Nk - 1);
@@ -213,18 +234,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(
     // The chunk swizzles of a loaded row do not depend on the round, so one
     // lane offset per tensor serves every round; rounds step by a scalar
     // offset (which the range check includes: out-of-range lanes write 0).
-    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-    const int ld_row = wave * C::RPW + lane / C::CH, ld_slot = lane % C::CH;
+    const int wave_s = wave_u;
+    const int ld_row = (SK > 1 ? wave_u : wave) * C::RPW + lane / C::CH, ld_slot = lane % C::CH;
     const int ld_voff_k = (ld_row * D + ((ld_slot ^ swz_k<D>(ld_row)) * 8)) * 2;
     const int ld_voff_v = (ld_row * D + ((ld_slot ^ swz_v<D>(ld_row)) * 8)) * 2;
-    constexpr int ROUND_BYTES = NW * C::RPW * D * 2;
+    constexpr int ROUND_BYTES = NWG * C::RPW * D * 2;
     auto dma_rows = [&](const __bf16 *base, int j0, __bf16 *dst, int voff) {
         const int rows_left = Nk - j0;
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(base + (size_t)j0 * D), (short)0, (rows_left < BN ? rows_left : BN) * D * 2, 0x00020000);
 #pragma unroll
         for (int r = 0; r < C::ROUNDS; ++r) {
-            __bf16 *d = dst + (r * NW + wave_s) * C::RPW * D;  // wave-uniform LDS destination
+            __bf16 *d = dst + (r * NWG + wave_s) * C::RPW * D;  // wave-uniform LDS destination
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)d, 16, voff, r * ROUND_BYTES, 0, 0);
         }
     };
@@ -299,19 +320,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(
     // are interleaved instruction by instruction below), then multiplies P by
     // V of tile j.  Loads run ahead: iteration j starts K[j+2] and V[j+1]
     // into the buffers iteration j-1 finished with.
-    auto kbuf = [&](int j) { return (j & 1) ? sK1 : sK0; };
-    auto vbuf = [&](int j) { return (j & 1) ? sV1 : sV0; };
-    auto dma_k = [&](int j) { dma_rows(Kh, j * BN, kbuf(j), ld_voff_k); };
-    auto dma_v = [&](int j) { dma_rows(Vh, j * BN, vbuf(j), ld_voff_v); };
+    // j counts the group's own tiles; its tile j is key tile tb + j
+    const int goff = SK > 1 ? grp * C::TILE : 0;
+    auto kbuf = [&](int j) { return ((j & 1) ? sK1 : sK0) + goff; };
+    auto vbuf = [&](int j) { return ((j & 1) ? sV1 : sV0) + goff; };
+    auto dma_k = [&](int j) { dma_rows(Kh, (tb + j) * BN, kbuf(j), ld_voff_k); };
+    auto dma_v = [&](int j) { dma_rows(Vh, (tb + j) * BN, vbuf(j), ld_voff_v); };
 
     // One pipeline iteration; cur holds S^T of tile j, nxt receives tile j+1.
     // Returns false when this wave is done (its rows see no later key).
     auto iteration = [&](const int j, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
-        const int j0 = j * BN;
+        const int j0 = (tb + j) * BN;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K[j+1] and V[j] have landed
         __syncthreads();                                   // ... for every wave; K[j], V[j-1] are free
-        if (j + 2 < ntiles) dma_k(j + 2);
-        if (j + 1 < ntiles) dma_v(j + 1);
+        if constexpr (SK > 1) {
+            if (j >= cnt) return;  // this group's tiles are done
+        }
+        if (j + 2 < cnt) dma_k(j + 2);
+        if (j + 1 < cnt) dma_v(j + 1);
         // waves whose rows see none of tile j skip it (and every later tile)
         if (CAUSAL && j0 > wave_first_row + 31 + off) return;
 
@@ -421,17 +447,65 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(
     };
 
     f32x16 stA[2], stB[2];
-    if (ntiles > 0) {
-        dma_k(0);
-        dma_v(0);
-        if (ntiles > 1) dma_k(1);
+    if (nit > 0) {
+        if (cnt > 0) {
+            dma_k(0);
+            dma_v(0);
+            if (cnt > 1) dma_k(1);
+        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        qk(sK0, stA);
+        if (cnt > 0) qk(kbuf(0), stA);
     }
-    for (int j = 0; j < ntiles; j += 2) {
+    for (int j = 0; j < nit; j += 2) {
         iteration(j, stA, stB);
-        if (j + 1 < ntiles) iteration(j + 1, stB, stA);
+        if (j + 1 < nit) iteration(j + 1, stB, stA);
+    }
+
+    // ---- key groups: merge the partial states through LDS -----------------
+    // Group g > 0 leaves (O^T, m_ref, l) of each lane in LDS; group 0 folds
+    // them in: with m = max(m_0, m_g), O^T and l of each side are scaled by
+    // 2^(m_side - m) and added (one more step of the online-softmax
+    // recurrence, applied to two key ranges).  Lanes keep their layout, so
+    // the merge is element-wise.
+    if constexpr (SK > 1) {
+        constexpr int NE = 16 * C::CB + 2;             // floats per lane
+        constexpr int ARR_F = SK * C::TILE / 2;         // floats per LDS array
+        constexpr int BPA = ARR_F / (NE * 64);          // per-wave blocks per array
+        static_assert(BPA * 4 >= (SK - 1) * NWG, "merge staging space");
+        auto blk = [&](int bi) -> float * {
+            const int ai = bi / BPA;
+            float *base = ai == 0 ? (float *)sK0 : ai == 1 ? (float *)sK1 : ai == 2 ? (float *)sV0 : (float *)sV1;
+            return base + (bi % BPA) * NE * 64 + lane;
+        };
+        __syncthreads();  // every group is done with its tiles
+        if (grp > 0) {
+            float *st = blk((grp - 1) * NWG + wave_u);
+#pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) st[(16 * cb + r) * 64] = acc[cb][r];
+            }
+            st[16 * C::CB * 64] = m_ref;
+            st[(16 * C::CB + 1) * 64] = l_run;
+        }
+        __syncthreads();
+        if (grp > 0) return;
+#pragma unroll 1
+        for (int g2 = 1; g2 < SK; ++g2) {
+            const float *st = blk((g2 - 1) * NWG + wave_u);
+            const float mg = st[16 * C::CB * 64], lg = st[(16 * C::CB + 1) * 64];
+            const float mn = fmaxf(m_ref, mg);
+            const float a0 = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mn);
+            const float ag = mg == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mg - mn);
+            l_run = l_run * a0 + lg * ag;
+#pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[cb][r] = acc[cb][r] * a0 + st[(16 * cb + r) * 64] * ag;
+            }
+            m_ref = mn;
+        }
     }
 
     // ---- epilogue: O = u / l, LSE = ln(sum exp(s)) -----------------------
@@ -455,16 +529,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(
     }
 }
 
-template <int D, bool CAUSAL, int NW, int HP>
+template <int D, bool CAUSAL, int NW, int HP, int SK = 1>
 hipError_t launch_nw(const FwdArgs &a, hipStream_t stream) {
-    using C = Cfg<D, NW>;
-    constexpr int BMP = 32 * (NW / HP);
+    constexpr int BMP = 32 * (NW / SK / HP);
     const float sl2 = a.scale * LOG2E;
     const int n_qtiles = (a.Nq + BMP - 1) / BMP;
     const long long total = (long long)a.B * (a.Hq / HP) * n_qtiles;
     if (total <= 0) return hipSuccess;
     if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, NW, HP>), dim3((unsigned)total), dim3(C::NTHR), 0, stream,
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, NW, HP, SK>), dim3((unsigned)total), dim3(64 * NW), 0, stream,
                        (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v, (__bf16 *)a.o,
                        a.lse, a.Hq, a.Hkv, a.Nq, a.Nk, sl2, n_qtiles, (int)total);
     return hipGetLastError();
@@ -476,6 +549,14 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream) {
     const hipError_t e = device_cu_count(&cus);
     if (e != hipSuccess) return e;
     const long long two_per_cu = 2LL * cus;
+    // causal grid of fewer 128-row workgroups than CUs: the deepest rows
+    // set the time, so their keys are split over the key groups of one
+    // 8-wave workgroup (64 rows x 4 groups for d = 64, 128 rows x 2 groups
+    // for d = 128, which needs twice the LDS per group)
+    if (CAUSAL && (long long)a.B * a.Hq * ((a.Nq + 127) / 128) < cus) {
+        if constexpr (D == 64) return launch_nw<D, CAUSAL, 8, 1, 4>(a, stream);
+        else return launch_nw<D, CAUSAL, 8, 1, 2>(a, stream);
+    }
     // 8-wave workgroups of 256 rows of one head when the rows see similar
     // numbers of keys and the grid still holds at least two of them per CU
     const bool even_rows = !CAUSAL || (long long)a.Nk - a.Nq >= a.Nq;

@@ -29,6 +29,21 @@ def gpu_fwd(q, k, v, scale, causal):
     return I.to_f64(o), I.to_f64(lse)
 
 
+def narrow_form_copies(Nq):
+    """Copies of one head that give the forward a grid of at least two
+    128-row workgroups per CU.  A causal grid of fewer than one per CU runs
+    the key-split form, which adds its sums in another order; copies of a
+    head in this many heads run the 4-wave 128-row form, whose row
+    arithmetic the wider forms share."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return -(-2 * cus // -(-Nq // 128))
+
+
+def one_head(t, b, h, copies):
+    """Head h of batch entry b as a [1, copies, N, d] tensor."""
+    return t[b:b + 1, h:h + 1].repeat(1, copies, 1, 1)
+
+
 def gpu_decode(seq_lens, q, kc, vc, scale, keys_per_split=0):
     """attn_decode (default split), or attn_decode_split for keys_per_split > 0."""
     if keys_per_split:

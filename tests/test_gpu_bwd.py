@@ -21,7 +21,7 @@ import torch
 
 import exact_scaled_dot_sdpa_amd as E
 from exact_scaled_dot_sdpa_amd import inputs as I
-from gpu_util import dev, grad_floors, say
+from gpu_util import dev, grad_floors, narrow_form_copies, one_head, say
 
 pytestmark = pytest.mark.gpu
 
@@ -172,14 +172,18 @@ def test_dq_workgroup_forms_agree(Nq, Nk, Hq, Hkv):
     heads (group of 4) that share a K/V head; one head alone is too small a
     grid for that and runs 4-wave workgroups of 128 rows; groups of 16 and 12
     take two and three blocks of heads.  Each row's arithmetic is the same in
-    both forms, so dq must agree bit for bit."""
+    both forms, so dq must agree bit for bit.  The single head is repeated as
+    separate heads so that its forward (whose O and LSE the backward reads)
+    also runs a form that shares the row arithmetic, not the key-split form
+    of very small grids."""
     B, d = 2, 128
     q, k, v, do = I.bwd_inputs(B, Hq, Hkv, Nq, Nk, d, "bf16", seed=91 + Nq)
     dq_all = gpu_fwd_bwd(q, k, v, do, 0.09, True)[0]
     G = Hq // Hkv
+    R = narrow_form_copies(Nq)
     for b, h in [(0, 0), (1, 37), (1, Hq - 1)]:
         hk = h // G
         say("[bwd forms] b=%d h=%d" % (b, h))
-        dq1 = gpu_fwd_bwd(q[b:b + 1, h:h + 1], k[b:b + 1, hk:hk + 1], v[b:b + 1, hk:hk + 1], do[b:b + 1, h:h + 1],
+        dq1 = gpu_fwd_bwd(one_head(q, b, h, R), one_head(k, b, hk, R), one_head(v, b, hk, R), one_head(do, b, h, R),
                           0.09, True)[0]
         assert np.array_equal(dq1[0, 0], dq_all[b, h]), (b, h)

@@ -5,7 +5,7 @@ import torch
 
 import exact_scaled_dot_sdpa_amd as E
 from exact_scaled_dot_sdpa_amd import inputs as I
-from gpu_util import TOL_LSE, TOL_O, assert_close, dev, gpu_fwd, max_err, say
+from gpu_util import TOL_LSE, TOL_O, assert_close, dev, gpu_fwd, max_err, narrow_form_copies, one_head, say
 
 pytestmark = pytest.mark.gpu
 
@@ -52,6 +52,10 @@ RAGGED = [
     ("bf16", 128, 1, 8, 1, 65, 129, True),     # MQA
     ("bf16", 64, 1, 16, 2, 129, 63, False),    # Nk < one tile
     ("bf16", 128, 1, 1, 1, 1000, 1000, True),
+    # key-split form: fewer key tiles than key groups, odd tile counts
+    ("bf16", 64, 1, 2, 1, 130, 130, True),
+    ("bf16", 128, 1, 3, 3, 90, 200, True),
+    ("bf16", 64, 2, 3, 1, 50, 700, True),      # chunked prefill
     # more work groups than the chip holds at once, ragged tails
     ("bf16", 128, 2, 64, 16, 1000, 1000, True),
     ("bf16", 64, 2, 128, 8, 700, 1100, True),    # chunked prefill
@@ -166,17 +170,43 @@ def test_wide_and_narrow_workgroups_agree(causal, Nq, Nk, Hq, Hkv):
     with rows at very different depths the same 32 query positions of the 8
     heads that share a K/V head (group of 8), or 64 positions of 4 heads
     (group of 4); groups of 16 and 12 take two and three such blocks of
-    heads.  One head alone is too small a grid for any of them and uses
-    128-row workgroups of 4 waves.  Each row's arithmetic is the same in every
-    form, so the outputs must agree bit for bit."""
+    heads.  Copies of one head as separate heads (MHA) are too few rows for
+    any of them and use 128-row workgroups of 4 waves.  Each row's arithmetic
+    is the same in every form, so the outputs must agree bit for bit."""
     B, d = 2, 128
     q, k, v = I.prefill_inputs(B, Hq, Hkv, Nq, Nk, d, "bf16", seed=61 + Nq)
     o_all, l_all = gpu_fwd(q, k, v, 0.09, causal)
     G = Hq // Hkv
+    R = narrow_form_copies(Nq)
     for b, h in [(0, 0), (1, 37), (1, Hq - 1)]:
         hk = h // G
-        o1, l1 = gpu_fwd(q[b:b + 1, h:h + 1], k[b:b + 1, hk:hk + 1], v[b:b + 1, hk:hk + 1], 0.09, causal)
+        o1, l1 = gpu_fwd(one_head(q, b, h, R), one_head(k, b, hk, R), one_head(v, b, hk, R), 0.09, causal)
         assert np.array_equal(o1[0, 0], o_all[b, h]) and np.array_equal(l1[0, 0], l_all[b, h]), (b, h)
+        assert np.array_equal(o1[0, R - 1], o1[0, 0]), (b, h)
+
+
+@pytest.mark.parametrize("d,Nq,Nk,causal", [(64, 1000, 1000, True), (128, 1000, 1000, True),
+                                            (64, 300, 900, True), (128, 257, 300, True)])
+def test_key_split_form_close_to_4wave_form(orc, d, Nq, Nk, causal):
+    """One causal head is a grid of fewer 128-row workgroups than CUs: its
+    key range is split over the key groups of one workgroup and the partial
+    states merged.  That changes only the order of the sums (and the points
+    where the reference of each part is raised), so the result stays within
+    the parity bound of the oracle and within a few bf16 units of the 4-wave
+    form of the same rows."""
+    q, k, v = I.prefill_inputs(1, 1, 1, Nq, Nk, d, "bf16", seed=71 + Nq + d)
+    scale = 1.0 / np.sqrt(d)
+    o1, l1 = gpu_fwd(q, k, v, scale, causal)
+    R = narrow_form_copies(Nq)
+    o4, l4 = gpu_fwd(one_head(q, 0, 0, R), one_head(k, 0, 0, R), one_head(v, 0, 0, R), scale, causal)
+    o_ref, lse_ref = orc.attn(I.to_f64(q), I.to_f64(k), I.to_f64(v), scale, causal)
+    assert_close("key-split O", o1, o_ref, TOL_O["bf16"])
+    assert_close("key-split LSE", l1, lse_ref, TOL_LSE)
+    # two bf16 units of the output's magnitude, plus the rounding of P
+    excess = float((np.abs(o1[0, 0] - o4[0, 0]) - (2.0 ** -8 + 2.0 ** -6 * np.abs(o4[0, 0]))).max())
+    say("  key-split vs 4-wave: max |diff| - bound = %.3e" % excess)
+    assert excess <= 0
+    assert_close("key-split vs 4-wave LSE", l1[0, 0], l4[0, 0], 1e-4)
 
 
 def test_run_twice_bitwise():
