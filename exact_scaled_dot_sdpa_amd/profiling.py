@@ -45,6 +45,25 @@ def _short(name):
     return name[:60]
 
 
+def _targs(name):
+    """The integer / bool template arguments of an Itanium-mangled kernel
+    name, as "<64,true,8>", or "" when it has none."""
+    short = _short(name)
+    i = name.find(short)
+    if not name.startswith("_Z") or i < 0 or name[i + len(short):i + len(short) + 1] != "I":
+        return ""
+    args = re.findall(r"L([ib])(n?\d+)E", name[i + len(short):].split("EE", 1)[0] + "E")
+    return "<%s>" % ",".join(("true" if v == "1" else "false") if t == "b" else v.replace("n", "-")
+                              for t, v in args)
+
+
+def _labels(names):
+    """Short names; where several kernels share one, each with its template
+    arguments."""
+    shorts = [_short(n) for n in names]
+    return {n: s + (_targs(n) if shorts.count(s) > 1 else "") for n, s in zip(names, shorts)}
+
+
 def _last_n(trace_csv, n):
     """(dispatches, median us, mean us) of the last n dispatches of each
     kernel in a rocprofv3 kernel_trace csv (the timed steps, after the
@@ -63,11 +82,12 @@ def _last_n(trace_csv, n):
 
 def stats(path, cmd, out, trace=None, last=0):
     rows = list(csv.DictReader(open(path)))
+    label = _labels([r["Name"] for r in rows])
     lines = ["# rocprofv3 kernel statistics", "", "Command:", "", "```", cmd, "```", "",
              "| kernel | calls | avg (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
     for r in rows:
         lines.append("| %s | %s | %.2f | %.2f | %.2f | %.2f%% |" % (
-            _short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            label[r["Name"]], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
     if trace and last > 0:
         timed = _last_n(trace, last)
@@ -75,8 +95,9 @@ def stats(path, cmd, out, trace=None, last=0):
                       "warm-up dispatches), from the kernel trace: the median is the primary figure, the mean "
                       "the one the bench line's HIP events compare with:" % last, "",
                   "| kernel | dispatches | median (us) | mean (us) |", "|---|---|---|---|"]
+        tl = _labels(list(timed))
         for name, (cnt, med, avg) in sorted(timed.items(), key=lambda kv: -kv[1][2]):
-            lines.append("| %s | %d | %.2f | %.2f |" % (_short(name), cnt, med, avg))
+            lines.append("| %s | %d | %.2f | %.2f |" % (tl[name], cnt, med, avg))
     lines += ["", "Full kernel names:", ""] + ["- `%s`" % r["Name"] for r in rows]
     text = "\n".join(lines) + "\n"
     with open(out, "w") as f:
@@ -228,7 +249,10 @@ def counters(csv_path, cmd, out, algorithmic=None, json_out=None):
             if len(found) != len(names) or not all(c > 0 and d > 0 for c, d, _ in found):
                 continue
             cyc, dur, busy = (sum(x[i] for x in found) for i in range(3))
-            kernels[logical] = {"clock_ghz": round(cyc / dur, 3), "mfma_busy": round(busy / cyc, 4),
+            # the cycle counters' window exceeds a short kernel's duration, so
+            # the clock is only recorded for long ones (as in the table above)
+            kernels[logical] = {"clock_ghz": round(cyc / dur, 3) if dur >= 100e3 else None,
+                                "mfma_busy": round(busy / cyc, 4),
                                 "duration_us": round(dur / 1e3, 2), "source_digest": source_digest(logical)}
         with open(json_out, "w") as f:
             json.dump({"command": cmd, "kernels": kernels}, f, indent=1)
