@@ -19,10 +19,12 @@
  *
  * Conventions shared by every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
- *     allocates nothing.  Its only global state is a per-device cache of two
+ *     allocates nothing.  Its global state is a per-device cache of two
  *     device properties (compute-unit count, decode occupancy), written once
- *     on first use with the value the runtime reports; it never changes a
- *     result, and calls on different streams or threads may run concurrently.
+ *     on first use with the value the runtime reports, which never changes a
+ *     result, and the fixed device array of attn_decode_noalloc (see there).
+ *     Calls on different streams or threads may run concurrently, except
+ *     attn_decode_noalloc calls on one device.
  *   - Tensors are contiguous, row-major, head dim innermost, 16-byte aligned
  *     (lse and seq_lens: 4-byte aligned).
  *   - Calls are asynchronous on `stream` (NULL = the null stream) and return
