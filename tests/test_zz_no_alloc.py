@@ -49,3 +49,38 @@ def test_noalloc_refuses_oversize():
     assert ei.value.status == E.ATTN_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert (o == 5.0).all().item()
+
+
+def test_noalloc_under_graph_capture():
+    """The use the entry point is for: a decode step captured in a HIP graph
+    with no workspace to allocate, replayed several times.  Between the
+    replays an eager call of another size reuses the same array and the
+    stream is synchronised; every replay and every eager call reproduces
+    attn_decode bit for bit."""
+    sl, q, kc, vc = (dev(t) for t in I.decode_inputs(4, 32, 8, 1024, 128, "bf16", seed=7003, lo=1, hi=1024))
+    s2, q2, k2, v2 = (dev(t) for t in I.decode_inputs(3, 8, 2, 700, 64, "bf16", seed=7004, lo=0, hi=700))
+    o_ref, lse_ref = E.attn_decode(q, kc, vc, sl, scale=0.088)
+    o2_ref, lse2_ref = E.attn_decode(q2, k2, v2, s2, scale=0.125)
+    o = torch.empty_like(q)
+    lse = torch.empty(4, 32, dtype=torch.float32, device="cuda")
+    o2 = torch.empty_like(q2)
+    lse2 = torch.empty(3, 8, dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up off the default stream before capture
+        E.attn_decode_noalloc(q, kc, vc, sl, o, lse, scale=0.088)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        E.attn_decode_noalloc(q, kc, vc, sl, o, lse, scale=0.088)
+    for rep in range(4):
+        say("[noalloc graph] replay %d" % rep)
+        o.zero_()
+        lse.zero_()
+        E.attn_decode_noalloc(q2, k2, v2, s2, o2, lse2, scale=0.125)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, o2_ref) and torch.equal(lse2, lse2_ref), "eager call %d" % rep
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref), "replay %d" % rep
