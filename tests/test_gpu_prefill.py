@@ -56,6 +56,8 @@ RAGGED = [
     ("bf16", 64, 1, 2, 1, 130, 130, True),
     ("bf16", 128, 1, 3, 3, 90, 200, True),
     ("bf16", 64, 2, 3, 1, 50, 700, True),      # chunked prefill
+    ("bf16", 128, 1, 2, 1, 1, 500, True),      # one query row over 8 key tiles, both groups busy
+    ("bf16", 64, 1, 2, 1, 40, 300, True),      # 5 key tiles over 4 groups: runs of 1, 1, 1, 2
     # more work groups than the chip holds at once, ragged tails
     ("bf16", 128, 2, 64, 16, 1000, 1000, True),
     ("bf16", 64, 2, 128, 8, 700, 1100, True),    # chunked prefill
