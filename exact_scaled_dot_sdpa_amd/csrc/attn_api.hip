@@ -14,7 +14,8 @@ static_assert(attn::DECODE_SCRATCH_BYTES == ATTN_DECODE_NOALLOC_MAX_BYTES,
 namespace {
 
 // Upper bound on the workgroups of the decode split kernel; the default
-// (keys_per_split == 0) uses as many as the device holds at once, at most this.
+// (keys_per_split == 0) uses two per CU for a contiguous cache and as many as
+// the device holds at once for a paged one, at most this.
 constexpr int DECODE_MAX_WG = 2048;
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }

@@ -11,9 +11,11 @@
 // Work partition.  A (sequence b, K/V head hk, block hb of up to 16 query heads
 // of the group) is one "segment" of seq_lens[b] keys; the segments are laid
 // end to end (b outer, then hk, then hb) into one list of T keys, which is cut
-// into n_wg equal ranges, one per single-wave workgroup.  With n_wg set to the
-// number of workgroups the chip holds at once, every workgroup streams the
-// same number of bytes whatever the length mix of the batch.  A range that
+// into n_wg equal ranges, one per single-wave workgroup.  With n_wg a whole
+// multiple of the CU count that the chip holds at once (by default two per CU
+// for a contiguous cache, three -- the occupancy limit -- for a paged one),
+// every workgroup streams the same number of bytes whatever the length mix
+// of the batch, and every CU the same number of workgroups.  A range that
 // covers a whole segment writes its output rows directly.  A range that
 // covers part of a segment writes a partial result (normalised output and
 // log-sum-exp of its keys) to the workspace; a second kernel merges the
@@ -647,21 +649,30 @@ template <int D, int QR, int NST>
 hipError_t launch_cfg(const DecodeArgs &a, hipStream_t stream) {
     int n_wg = a.n_wg;
     if (n_wg <= 0) {
-        // as many single-wave workgroups as the chip holds at once (queried
-        // once per device; concurrent first calls store the same value)
-        static std::atomic<int> cached[64];
+        // As many single-wave workgroups as the chip holds at once for a
+        // paged cache, and at most two per CU for a contiguous one (the CU
+        // count and occupancy are queried once per device; concurrent first
+        // calls store the same values).  Timed interleaved on the decode
+        // workload: contiguous, two per CU beat three (the occupancy limit)
+        // by 1.5-2 %; paged, three per CU beat two by 4-5 % at block sizes
+        // 64-256 and by 21 % at 16, its extra waves hiding the block-table
+        // lookups; counts that are not a multiple of the CU count were slower.
+        static std::atomic<int> cached_cus[64], cached_per_cu[64];
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-        n_wg = cached[dev].load(std::memory_order_relaxed);
-        if (n_wg == 0) {
-            int cus = 0, per_cu = 0;
+        int cus = cached_cus[dev].load(std::memory_order_relaxed);
+        int per_cu = cached_per_cu[dev].load(std::memory_order_relaxed);
+        if (cus == 0 || per_cu == 0) {
             hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
             if (e != hipSuccess) return e;
             e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_chunk_kernel<D, QR, NST>, 64, 0);
             if (e != hipSuccess) return e;
-            n_wg = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
-            cached[dev].store(n_wg, std::memory_order_relaxed);
+            cus = cus > 0 ? cus : 1;
+            per_cu = per_cu > 0 ? per_cu : 1;
+            cached_cus[dev].store(cus, std::memory_order_relaxed);
+            cached_per_cu[dev].store(per_cu, std::memory_order_relaxed);
         }
+        n_wg = cus * (a.block_table || per_cu < 2 ? per_cu : 2);
     }
     if (n_wg > a.max_wg) n_wg = a.max_wg;
     const float sl2 = a.scale * LOG2E;

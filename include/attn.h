@@ -205,7 +205,8 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_seq_len,
  * cached keys and values); this equals the last row of causal attn_fwd over
  * those rows.  The cache is not appended to.  The valid keys of all
  * (sequence, K/V head, block of 16 query heads) are laid end to end and cut
- * into equal ranges, one per workgroup, as many as the device holds at once;
+ * into equal ranges, one per workgroup, two per compute unit (fewer if the
+ * device holds fewer at once; attn_decode_paged: as many as it holds);
  * the partial results of blocks that several ranges share are merged through
  * their log-sum-exps ("从注意力到 IO 感知执行", sec. 8, eqs. (1)-(2), applied
  * to whole ranges).  A sequence with seq_lens[b] == 0 gets O = 0 and
@@ -229,8 +230,8 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache,
  * an explicit split: keys_per_split > 0 asks for ranges of about that many
  * keys of the max_seq_len-sized cache, i.e. W = ceil(B * Hkv * ceil(G / 16) *
  * max_seq_len / keys_per_split) workgroups clamped to [1, 2048];
- * keys_per_split == 0 is attn_decode's default (as many workgroups as the
- * device holds at once).  The workspace then has S = B * Hkv * ceil(G / 16) +
+ * keys_per_split == 0 is the default of attn_decode (two workgroups per
+ * compute unit) or attn_decode_paged (as many as the device holds at once).  The workspace then has S = B * Hkv * ceil(G / 16) +
  * W - 1 slots (W = 2048 for keys_per_split == 0), laid out as for
  * attn_decode.  Everything else is attn_decode's.  The result is the same up
  * to the order of floating-point sums (split invariance).

@@ -2,8 +2,8 @@
 
 The split kernel cuts the keys of the whole batch (every sequence, K/V head
 and block of 16 query heads laid end to end) into equal ranges, one per
-workgroup; keys_per_split sets the range length (0: one range per workgroup
-the device holds at once).  The cases below cover ranges shorter than a
+workgroup; keys_per_split sets the range length (0: two ranges per compute
+unit).  The cases below cover ranges shorter than a
 chunk, ranges that span many short sequences, several pages of 64 sequences,
 empty sequences and workgroups whose range is empty."""
 import numpy as np
