@@ -67,7 +67,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50,
                     help="untimed steps first (the GPU clock settles within about 50 ms of load)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target seconds of oracle work")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="target seconds of oracle work (the small calibration sample runs slower per row, "
+                         "so the sample lands at about two thirds of this)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--only", choices=["prefill", "decode", "bwd", "fp8"], default=None,
