@@ -147,18 +147,32 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(
     __shared__ __attribute__((aligned(1024))) __bf16 sV1[SK * C::TILE];
 
     // ---- work item: XCD-contiguous remap of the linear block id ----------
+    // (key-split form: blocks in dispatch order, the query tiles of every
+    // head heaviest first, so that the workgroups that wait for a free CU
+    // are the light ones; these grids are small and share no K/V across heads)
     const int L = blockIdx.x;
     const int xcd = L & 7, local = L >> 3;
     const int per = total >> 3, rem = total & 7;
-    const int w = xcd * per + (xcd < rem ? xcd : rem) + local;
+    const int w = SK > 1 ? L : xcd * per + (xcd < rem ? xcd : rem) + local;
     const int G = Hq / Hkv;
     const int nhb = G / HP;
-    const int gqb = w % nhb;
-    int t = w / nhb;
-    const int tq_ord = t % n_qtiles;
-    t /= n_qtiles;
-    const int hk = t % Hkv;
-    const int b = t / Hkv;
+    int gqb, tq_ord, hk, b;
+    if constexpr (SK > 1) {
+        const int per_tile = total / n_qtiles;  // (batch, K/V head, head block) items per query tile
+        tq_ord = w / per_tile;
+        int t = w - tq_ord * per_tile;
+        gqb = t % nhb;
+        t /= nhb;
+        hk = t % Hkv;
+        b = t / Hkv;
+    } else {
+        gqb = w % nhb;
+        int t = w / nhb;
+        tq_ord = t % n_qtiles;
+        t /= n_qtiles;
+        hk = t % Hkv;
+        b = t / Hkv;
+    }
     const int tq = CAUSAL ? (n_qtiles - 1 - tq_ord) : tq_ord;
     const int q0 = tq * BMP;
 
