@@ -235,14 +235,28 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
     // tile first), then the blocks of HP query heads of the group; the NW
     // waves cover HP heads at BMP query positions
     constexpr int BMP = 32 * (NW / HP);
-    const int w = xcd_remap(blockIdx.x, total);
+    // (causal layers with one query head per K/V head: blocks in dispatch
+    // order, query tiles heaviest first across all heads, as in the forward)
     const int G = Hq / Hkv;
+    const bool flat = CAUSAL && G == 1;
+    const int w = flat ? (int)blockIdx.x : xcd_remap(blockIdx.x, total);
     const int nhb = G / HP;
-    const int gqb = w % nhb;
-    int t = w / nhb;
-    const int tq_ord = t % n_qtiles;
-    t /= n_qtiles;
-    const int hk = t % Hkv, b = t / Hkv;
+    int gqb, tq_ord, hk, b;
+    if (flat) {
+        const int per_tile = total / n_qtiles;
+        tq_ord = w / per_tile;
+        const int t = w - tq_ord * per_tile;  // nhb == 1
+        gqb = 0;
+        hk = t % Hkv;
+        b = t / Hkv;
+    } else {
+        gqb = w % nhb;
+        int t = w / nhb;
+        tq_ord = t % n_qtiles;
+        t /= n_qtiles;
+        hk = t % Hkv;
+        b = t / Hkv;
+    }
     const int q0 = (CAUSAL ? (n_qtiles - 1 - tq_ord) : tq_ord) * BMP;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -422,11 +436,15 @@ __global__ __launch_bounds__(KNW * 64) void bwd_dkdv_kernel(
 
     // work item: (batch, KV head) outermost, then key tile (heaviest causal
     // tile, the first, first)
-    const int w = xcd_remap(blockIdx.x, total);
-    const int tk = w % n_ktiles;
-    const int bh = w / n_ktiles;
-    const int hk = bh % Hkv, b = bh / Hkv;
+    // (causal layers with one query head per K/V head: blocks in dispatch
+    // order, key tiles heaviest first across all heads)
     const int G = Hq / Hkv;
+    const bool flat = CAUSAL && G == 1;
+    const int w = flat ? (int)blockIdx.x : xcd_remap(blockIdx.x, total);
+    const int per_tile = total / n_ktiles;
+    const int tk = flat ? w / per_tile : w % n_ktiles;
+    const int bh = flat ? w - tk * per_tile : w / n_ktiles;
+    const int hk = bh % Hkv, b = bh / Hkv;
     const int k0 = tk * BKN;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
