@@ -231,10 +231,11 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache,
  * keys of the max_seq_len-sized cache, i.e. W = ceil(B * Hkv * ceil(G / 16) *
  * max_seq_len / keys_per_split) workgroups clamped to [1, 2048];
  * keys_per_split == 0 is the default of attn_decode (two workgroups per
- * compute unit) or attn_decode_paged (as many as the device holds at once).  The workspace then has S = B * Hkv * ceil(G / 16) +
- * W - 1 slots (W = 2048 for keys_per_split == 0), laid out as for
- * attn_decode.  Everything else is attn_decode's.  The result is the same up
- * to the order of floating-point sums (split invariance).
+ * compute unit) or attn_decode_paged (as many as the device holds at once).
+ * The workspace then has S = B * Hkv * ceil(G / 16) + W - 1 slots (W = 2048
+ * for keys_per_split == 0), laid out as for attn_decode.  Everything else is
+ * attn_decode's.  The result is the same up to the order of floating-point
+ * sums (split invariance).
  */
 size_t attn_decode_split_workspace_bytes(int B, int Hq, int Hkv,
                                          int max_seq_len, int d,
