@@ -69,6 +69,7 @@ CASES = [
     (128, 2, 16, 4, 520, 700, True),   # GQA chunked, ragged tails on both sides
     (64, 2, 8, 8, 300, 257, False),
     (64, 1, 4, 1, 640, 640, True),
+    (128, 3, 6, 6, 300, 400, True),    # one query head per K/V head: tiles heaviest first across batch and heads
 ]
 
 

@@ -58,6 +58,9 @@ RAGGED = [
     ("bf16", 64, 2, 3, 1, 50, 700, True),      # chunked prefill
     ("bf16", 128, 1, 2, 1, 1, 500, True),      # one query row over 8 key tiles, both groups busy
     ("bf16", 64, 1, 2, 1, 40, 300, True),      # 5 key tiles over 4 groups: runs of 1, 1, 1, 2
+    # causal, one query head per K/V head: tiles dispatched heaviest first across batch and heads
+    ("bf16", 128, 3, 5, 5, 300, 300, True),    # key-split form
+    ("bf16", 64, 2, 40, 40, 400, 400, True),   # 4-wave form
     # more work groups than the chip holds at once, ragged tails
     ("bf16", 128, 2, 64, 16, 1000, 1000, True),
     ("bf16", 64, 2, 128, 8, 700, 1100, True),    # chunked prefill
