@@ -575,7 +575,7 @@ def main():
         out["roofline_decode"] = {
             "bound": "hbm", "achieved": round(d_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(d_gbs / PEAK_HBM_GBS, 4), "traffic": tr,
-            "kernel": "decode_chunk_kernel<128,4,3> + decode_merge_kernel<128>", "avg_launch_ms": round(d_ms, 5),
+            "kernel": "decode_chunk_kernel<__bf16,128,4,3> + decode_merge_kernel<__bf16,128>", "avg_launch_ms": round(d_ms, 5),
             "median_launch_ms": round(d_med, 5),
         }
     out["startup"] = dict(startup, note="library load and the first call of each kernel (code-object load "

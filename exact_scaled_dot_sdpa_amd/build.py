@@ -27,7 +27,7 @@ def sources():
 # The sources each logical kernel is built from (csrc/ file names).
 KERNEL_SOURCES = {
     "prefill": ("prefill_bf16.hip", "kernels.h"),
-    "decode": ("decode_bf16.hip", "kernels.h"),
+    "decode": ("decode.hip", "kernels.h"),
     "bwd": ("bwd_bf16.hip", "kernels.h"),
     "fp8": ("prefill_fp8.hip", "kernels.h"),
 }

@@ -171,7 +171,7 @@ int decode_call(const void *q, const void *k_cache, const void *v_cache, const i
     if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
     if (keys_per_split < 0) return ATTN_ERR_INVALID_ARG;
-    if (!supported_d(d) || dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;
     if (!q || !o || !seq_lens || !k_cache || !v_cache) return ATTN_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(o, 16) || !aligned(seq_lens, 4) || !aligned(k_cache, 16) ||
         !aligned(v_cache, 16))
@@ -196,8 +196,8 @@ int decode_call(const void *q, const void *k_cache, const void *v_cache, const i
 
     attn::DecodeArgs a{q, k_cache, v_cache, seq_lens, o, lse, B, Hq, Hkv, Lmax, d, scale,
                        p.nhb, p.n_wg, p.max_wg, (float *)workspace, (float *)((char *)workspace + ob),
-                       block_table, block_size, max_blocks, num_blocks};
-    const hipError_t e = attn::launch_decode_bf16(a, stream);
+                       block_table, block_size, max_blocks, num_blocks, dtype == ATTN_F32 ? 1 : 0};
+    const hipError_t e = attn::launch_decode(a, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

@@ -1,4 +1,4 @@
-// decode_bf16.hip -- one-token decode against a bf16 KV cache.
+// decode.hip -- one-token decode against a bf16 or fp32 KV cache.
 //
 // Each query of the new token attends to the first seq_lens[b] cached rows of
 // its K/V head ("Transformer 笔记：注意力机制为什么会变成系统问题", KV-cache
@@ -49,11 +49,23 @@
 //     (d = 64) 16x16 fp32 tiles.
 //   * LDS rows are XOR-swizzled per 16-byte chunk so that both operand reads
 //     are free of bank conflicts.
+//
+// fp32 caches (full-precision checks) take the same walk, ring and merge with
+// fp32 products throughout: the scores and P V run on
+// v_mfma_f32_16x16x4_f32, whose 16 x 16 result has the layout of the bf16
+// kernel's (lane: 4 keys of one head), so the softmax code is shared.  For the
+// scores each lane reads 4 consecutive d-values of its key (A) and of its head
+// (B) with one ds_read_b128 and feeds them to 4 MFMAs (the d-order of a dot
+// product is free).  P stays fp32 (no bf16 rounding anywhere); the V^T
+// operand of key 16 t + 4 g + i is read row-wise, 4 columns per lane and
+// ds_read_b128, and the 16 x 16 output blocks cover the columns in the order
+// that this read gives (block 4 h + e, row m <-> column 64 h + 4 m + e).
 #include "kernels.h"
 
 #include <math.h>
 
 #include <atomic>
+#include <type_traits>
 
 namespace attn {
 namespace {
@@ -82,40 +94,49 @@ constexpr float LOG2E = 1.44269504088896340736f;
 // reference; below it every p <= 2^24 and fp32 keeps its relative precision.
 constexpr float RESCALE_SUM = 16777216.f;
 
-template <int D>
+// ET: element type of q, the caches and o (__bf16 or float).
+template <typename ET, int D>
 struct DC {
-    static constexpr int CH = D / 8;                // 16-byte chunks per row
-    static constexpr int RPI = 64 / CH;             // rows per 1 KB load instruction
-    static constexpr int KI = CK / RPI;             // load instructions per K (or V) chunk
-    static constexpr int PER = 16 / RPI;            // instructions after which the swizzle repeats
-    static constexpr int KS = D / 32;               // k-steps of the score MFMA
-    static constexpr int CB = D / 16;               // 16-column blocks of O^T
-    static constexpr int CHUNK_BYTES = CK * D * 2;  // one K or V chunk
+    static constexpr bool F32 = sizeof(ET) == 4;
+    static constexpr int ROWB = D * (int)sizeof(ET);  // bytes per row
+    static constexpr int CH = ROWB / 16;             // 16-byte chunks per row
+    static constexpr int RPI = 64 / CH;              // rows per 1 KB load instruction
+    static constexpr int KI = CK / RPI;              // load instructions per K (or V) chunk
+    static constexpr int PER = 16 / RPI;             // instructions after which the swizzle repeats
+    static constexpr int KS = D / 32;                // k-steps of the bf16 score MFMA
+    static constexpr int CB = D / 16;                // 16-column blocks of O^T
+    static constexpr int CHUNK_BYTES = CK * ROWB;    // one K or V chunk
 };
 
 // Stage layout in LDS: K chunk, V chunk, query rows of the chunk's segment.
-template <int D, int QR>
+template <typename ET, int D, int QR>
 struct Stage {
-    using C = DC<D>;
+    using C = DC<ET, D>;
     static constexpr int QROWS = (QR + C::RPI - 1) / C::RPI * C::RPI;
     static constexpr int QI = QROWS / C::RPI;  // load instructions for the query rows
     static constexpr int K_OFF = 0;
     static constexpr int V_OFF = C::CHUNK_BYTES;
     static constexpr int Q_OFF = 2 * C::CHUNK_BYTES;
-    static constexpr int BYTES = Q_OFF + QROWS * D * 2;
+    static constexpr int BYTES = Q_OFF + QROWS * C::ROWB;
     static constexpr int NI = 2 * C::KI + QI;  // load instructions per chunk
     static_assert(BYTES % 1024 == 0, "stage alignment");
     static_assert((QROWS & (QROWS - 1)) == 0 && QROWS <= 16, "query rows: power of two up to 16");
 };
 
 // XOR swizzles of the 16-byte chunk index within a row (see the operand reads
-// for the access patterns they serve).
-template <int D> __device__ __forceinline__ int swz_k(int row);
-template <> __device__ __forceinline__ int swz_k<128>(int row) { return row & 15; }
-template <> __device__ __forceinline__ int swz_k<64>(int row) { return (row >> 1) & 7; }
-template <int D> __device__ __forceinline__ int swz_v(int row);
-template <> __device__ __forceinline__ int swz_v<128>(int row) { return (row & 7) << 1; }
-template <> __device__ __forceinline__ int swz_v<64>(int row) { return ((row >> 1) & 3) << 1; }
+// for the access patterns they serve).  fp32 rows (16 or 32 chunks): 16
+// consecutive rows read at one chunk index land on 16 different 16-byte bank
+// slots, and so do the 16 lanes that read chunks 0..15 (+16 h) of one row.
+template <typename ET, int D> __device__ __forceinline__ int swz_k(int row) {
+    if constexpr (sizeof(ET) == 4) return row & 15;
+    else if constexpr (D == 128) return row & 15;
+    else return (row >> 1) & 7;
+}
+template <typename ET, int D> __device__ __forceinline__ int swz_v(int row) {
+    if constexpr (sizeof(ET) == 4) return row & 15;
+    else if constexpr (D == 128) return (row & 7) << 1;
+    else return ((row >> 1) & 3) << 1;
+}
 
 __device__ __forceinline__ int clamp_len(int L, int Lmax) { return L < 0 ? 0 : (L > Lmax ? Lmax : L); }
 
@@ -148,12 +169,12 @@ __device__ __forceinline__ long long range_start(long long w, long long T, int n
 // range, the rest of the chunk reads as zeros) and the query rows of the
 // segment (q_bytes in range).  voff_*: per-lane byte offsets within a 1 KB
 // load, one per swizzle phase.
-template <int D, int QR>
-__device__ __forceinline__ void dma_chunk(char *dst, const __bf16 *k, const __bf16 *v, const __bf16 *q, int kv_bytes,
-                                          int q_bytes, const int (&voff_k)[DC<D>::PER],
-                                          const int (&voff_v)[DC<D>::PER]) {
-    using C = DC<D>;
-    using S = Stage<D, QR>;
+template <typename ET, int D, int QR>
+__device__ __forceinline__ void dma_chunk(char *dst, const ET *k, const ET *v, const ET *q, int kv_bytes, int q_bytes,
+                                          const int (&voff_k)[DC<ET, D>::PER],
+                                          const int (&voff_v)[DC<ET, D>::PER]) {
+    using C = DC<ET, D>;
+    using S = Stage<ET, D, QR>;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)k, (short)0, kv_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)v, (short)0, kv_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)q, (short)0, q_bytes, 0x00020000);
@@ -180,8 +201,8 @@ __device__ __forceinline__ void dma_chunk(char *dst, const __bf16 *k, const __bf
 // exp(lse_w), o = sum_w exp(lse_w - lse) o_w over the workgroups w0..w1 with
 // a non-empty range, i.e. one more step of the online-softmax recurrence
 // applied to whole key ranges.  Writes the gblk output rows from head0.
-template <int D>
-__device__ void merge_segment(const float *ws_o, const float *ws_lse, __bf16 *O, float *LSE, int seg, int w0, int w1,
+template <typename OT, int D>
+__device__ void merge_segment(const float *ws_o, const float *ws_lse, OT *O, float *LSE, int seg, int w0, int w1,
                               size_t head0, int gblk, int GB, long long T, int n_wg, int lane) {
     constexpr int C4 = D / 4;  // float4 groups per output row
     constexpr int RO = 2;      // outputs (float4) per lane per round
@@ -244,7 +265,10 @@ __device__ void merge_segment(const float *ws_o, const float *ws_lse, __bf16 *O,
         for (int r = 0; r < RO; ++r) {
             if (!act[r]) continue;
             const f32x4 res = o[r] * (1.f / sum[r]);
-            *reinterpret_cast<bf16x4 *>(O + (head0 + h[r]) * D + 4 * c4[r]) = __builtin_convertvector(res, bf16x4);
+            if constexpr (sizeof(OT) == 4)
+                *reinterpret_cast<f32x4 *>(O + (head0 + h[r]) * D + 4 * c4[r]) = res;
+            else
+                *reinterpret_cast<bf16x4 *>(O + (head0 + h[r]) * D + 4 * c4[r]) = __builtin_convertvector(res, bf16x4);
             if (LSE && c4[r] == 0) LSE[head0 + h[r]] = M[r] + __logf(sum[r]);
         }
     }
@@ -254,15 +278,15 @@ __device__ void merge_segment(const float *ws_o, const float *ws_lse, __bf16 *O,
 // [num_blocks, Hkv, bs, d] and row j of sequence b lives in block
 // block_table[b * max_blocks + j / bs] (entries clamped to the pool), row
 // j % bs; otherwise Kc / Vc are [B, Hkv, Lmax, d].
-template <int D, int QR, int NST>
+template <typename ET, int D, int QR, int NST>
 __global__ __launch_bounds__(64) void decode_chunk_kernel(
-    const __bf16 *__restrict__ Q, const __bf16 *__restrict__ Kc, const __bf16 *__restrict__ Vc,
-    const int32_t *__restrict__ seq_lens, __bf16 *__restrict__ O, float *__restrict__ LSE, float *__restrict__ ws_o,
-    float *__restrict__ ws_lse, int B, int Hq, int Hkv, int Lmax, int nhb, int n_wg, float sl2,
-    const int32_t *__restrict__ block_table, int bs, int max_blocks, int num_blocks)
+    const ET *__restrict__ Q, const ET *__restrict__ Kc, const ET *__restrict__ Vc, const int32_t *__restrict__ seq_lens,
+    ET *__restrict__ O, float *__restrict__ LSE, float *__restrict__ ws_o, float *__restrict__ ws_lse, int B, int Hq,
+    int Hkv, int Lmax, int nhb, int n_wg, float sl2, const int32_t *__restrict__ block_table, int bs,
+    int max_blocks, int num_blocks)
 {
-    using C = DC<D>;
-    using S = Stage<D, QR>;
+    using C = DC<ET, D>;
+    using S = Stage<ET, D, QR>;
     // one LDS array per stage: the compiler then knows which in-flight
     // LDS-DMA a stage's reads depend on instead of waiting for all of them
     __shared__ __attribute__((aligned(1024))) char lds0[S::BYTES];
@@ -293,8 +317,8 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
     for (int bz = w; bz < B; bz += n_wg) {
         const int L = bz < 64 ? __builtin_amdgcn_readlane(pageL, bz) : clamp_len(seq_lens[bz], Lmax);
         if (L == 0) {
-            __bf16 *dst = O + (size_t)bz * Hq * D;
-            for (int i = lane; i < Hq * D / 8; i += 64) *reinterpret_cast<u32x4 *>(dst + 8 * i) = u32x4{};
+            char *dst = reinterpret_cast<char *>(O + (size_t)bz * Hq * D);
+            for (int i = lane; i < Hq * C::ROWB / 16; i += 64) *reinterpret_cast<u32x4 *>(dst + 16 * i) = u32x4{};
             if (LSE)
                 for (int i = lane; i < Hq; i += 64) LSE[(size_t)bz * Hq + i] = -INFINITY;
         }
@@ -341,8 +365,8 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
 #pragma unroll
     for (int i = 0; i < C::PER; ++i) {
         const int R = i * C::RPI + ld_q;
-        voff_k[i] = ld_q * D * 2 + ((ld_p ^ swz_k<D>(R)) * 16);
-        voff_v[i] = ld_q * D * 2 + ((ld_p ^ swz_v<D>(R)) * 16);
+        voff_k[i] = ld_q * C::ROWB + ((ld_p ^ swz_k<ET, D>(R)) * 16);
+        voff_v[i] = ld_q * C::ROWB + ((ld_p ^ swz_v<ET, D>(R)) * 16);
     }
 
     // per-stage chunk records (wave-uniform): segment, key count, heads,
@@ -393,8 +417,8 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
         } else {
             row0 = (size_t)(b * Hkv + hk) * Lmax + key;
         }
-        dma_chunk<D, QR>(stage(st), Kc + row0 * D, Vc + row0 * D,
-                         Q + ((size_t)b * Hq + hk * G + 16 * hb) * D, cnt * D * 2, gblk * D * 2, voff_k, voff_v);
+        dma_chunk<ET, D, QR>(stage(st), Kc + row0 * D, Vc + row0 * D, Q + ((size_t)b * Hq + hk * G + 16 * hb) * D,
+                            cnt * C::ROWB, gblk * C::ROWB, voff_k, voff_v);
         m_seg[st] = b * nsub + sub;
         m_cnt[st] = cnt;
         m_gblk[st] = gblk;
@@ -429,25 +453,37 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
 
     // ---- operand read offsets (bytes), fixed for the kernel --------------
     const int n = lane & 15, g = lane >> 4;
-    // K (A operand, m = key n of a 16-key half) and Q (B operand, n = head):
-    // row n, chunk 4 kk + g; a half-chunk t adds 16 rows (same swizzle).
-    int k_off[C::KS], q_off[C::KS];
     const int qn = n & (S::QROWS - 1);  // Q slot row read by this lane (lanes past QROWS get zeros)
+    // bf16.  K (A operand, m = key n of a 16-key half) and Q (B operand, n =
+    // head): row n, chunk 4 kk + g; a half-chunk t adds 16 rows (same
+    // swizzle).  V (transposing reads): a 16-lane group g reads keys 4g ..
+    // 4g+3 (+16 for the second half) x 16 columns of block cb; this lane's 8
+    // bytes are key 4g + (n >> 2), columns 16 cb + 4 (n & 3) .. + 3.
+    // fp32.  K and Q: row n (qn), chunk 4 kk + g for kk < D / 16, d-values
+    // 16 kk + 4 g .. + 3 feeding 4 MFMAs; a half-chunk adds 16 rows.  V: key
+    // 16 t + 4 g + i, chunk n + 16 h (columns 64 h + 4 n .. + 3).
+    constexpr int NKO = C::F32 ? D / 16 : C::KS;  // K / Q operand reads per 16-key half
+    constexpr int NVO = C::F32 ? 4 * (D / 64) : C::CB;
+    int k_off[NKO], q_off[NKO], v_off[NVO];
 #pragma unroll
-    for (int kk = 0; kk < C::KS; ++kk) {
-        k_off[kk] = n * D * 2 + (((4 * kk + g) ^ swz_k<D>(n)) * 16);
-        q_off[kk] = qn * D * 2 + (((4 * kk + g) ^ swz_k<D>(qn)) * 16);
+    for (int kk = 0; kk < NKO; ++kk) {
+        k_off[kk] = n * C::ROWB + (((4 * kk + g) ^ swz_k<ET, D>(n)) * 16);
+        q_off[kk] = qn * C::ROWB + (((4 * kk + g) ^ swz_k<ET, D>(qn)) * 16);
     }
-    // V (transposing reads): a 16-lane group g reads keys 4g .. 4g+3 (+16 for
-    // the second half) x 16 columns of block cb; this lane's 8 bytes are key
-    // 4g + (n >> 2), columns 16 cb + 4 (n & 3) .. + 3.
-    int v_off[C::CB];
-    {
+    if constexpr (C::F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * g + i;  // + 16 t, same swizzle
+#pragma unroll
+            for (int h = 0; h < D / 64; ++h)
+                v_off[i * (D / 64) + h] = row * C::ROWB + (((n + 16 * h) ^ swz_v<ET, D>(row)) * 16);
+        }
+    } else {
         const int row = 4 * g + (n >> 2);
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb) {
             const int col = 16 * cb + 4 * (n & 3);
-            v_off[cb] = row * D * 2 + ((((col >> 3) ^ swz_v<D>(row))) * 16) + (col & 7) * 2;
+            v_off[cb] = row * C::ROWB + ((((col >> 3) ^ swz_v<ET, D>(row))) * 16) + (col & 7) * 2;
         }
     }
 
@@ -457,45 +493,122 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
     for (int cb = 0; cb < C::CB; ++cb) acc[cb] = f32x4{};
     float m_ref = 0.f, l_run = 0.f;
 
-    auto compute = [&](const int st) {
-        const char *src = stage(st);
-        const int cnt = m_cnt[st];
-        // operands
-        bf16x8 qb[C::KS];
+    // Operands of one chunk, all read from LDS before the first MFMA:
+    // Q / K (bf16x8 or 4 fp32 d-values per read) and V^T (bf16: transposing
+    // reads; fp32: 4 columns of key 16 t + 4 g + i, index (t, i, h)).
+    using Op = typename std::conditional<C::F32, f32x4, bf16x8>::type;
+    constexpr int NV = C::F32 ? 8 * (D / 64) : C::CB;
+    auto read_ops = [&](const char *src, Op (&qo)[NKO], Op (&ko)[2][NKO], Op (&vo)[NV]) {
 #pragma unroll
-        for (int kk = 0; kk < C::KS; ++kk) {
-            u32x4 x = *reinterpret_cast<const u32x4 *>(src + S::Q_OFF + q_off[kk]);
-            if (neg) x ^= 0x80008000u;
-            if (S::QROWS < 16 && n >= S::QROWS) x = u32x4{};  // heads beyond the stored rows
-            qb[kk] = __builtin_bit_cast(bf16x8, x);
+        for (int kk = 0; kk < NKO; ++kk) {
+            u32x4 qx = *reinterpret_cast<const u32x4 *>(src + S::Q_OFF + q_off[kk]);
+            if (neg) qx ^= C::F32 ? 0x80000000u : 0x80008000u;
+            if (S::QROWS < 16 && n >= S::QROWS) qx = u32x4{};  // heads beyond the stored rows
+            qo[kk] = __builtin_bit_cast(Op, qx);
         }
-        bf16x8 ka[2][C::KS];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int kk = 0; kk < C::KS; ++kk)
-                ka[t][kk] = *reinterpret_cast<const bf16x8 *>(src + S::K_OFF + t * 16 * D * 2 + k_off[kk]);
-        bf16x8 va[C::CB];
+            for (int kk = 0; kk < NKO; ++kk)
+                ko[t][kk] = *reinterpret_cast<const Op *>(src + S::K_OFF + t * 16 * C::ROWB + k_off[kk]);
+        if constexpr (C::F32) {
 #pragma unroll
-        for (int cb = 0; cb < C::CB; ++cb) {
-            i16x4 part[2];
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-                part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4 *)(src + S::V_OFF + h * 16 * D * 2 + v_off[cb]));
-            va[cb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                for (int j = 0; j < NVO; ++j)
+                    vo[t * NVO + j] = *reinterpret_cast<const f32x4 *>(src + S::V_OFF + t * 16 * C::ROWB + v_off[j]);
+        } else {
+#pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb) {
+                i16x4 part[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4 *)(src + S::V_OFF + h * 16 * C::ROWB + v_off[cb]));
+                vo[cb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            }
         }
-        // scores: lane holds head n, keys 16 t + 4 g + r
+    };
+
+    // Scores of a chunk: x[4 t + r] = q_n . k_(16 t + 4 g + r) (raw, unscaled).
+    auto scores = [&](const Op (&qo)[NKO], const Op (&ko)[2][NKO], float (&x)[8]) {
         f32x4 s[2] = {f32x4{}, f32x4{}};
 #pragma unroll
-        for (int kk = 0; kk < C::KS; ++kk)
+        for (int kk = 0; kk < NKO; ++kk)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t][kk], qb[kk], s[t], 0, 0, 0);
-        float x[8];
+            for (int t = 0; t < 2; ++t) {
+                if constexpr (C::F32) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        s[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ko[t][kk][e], qo[kk][e], s[t], 0, 0, 0);
+                } else {
+                    s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ko[t][kk], qo[kk], s[t], 0, 0, 0);
+                }
+            }
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) x[4 * t + r] = s[t][r];
+    };
+
+    // O^T += V^T P^T for a chunk; p[4 t + r] belongs to key 16 t + 4 g + r.
+    auto pv = [&](const Op (&vo)[NV], const float (&p)[8]) {
+        if constexpr (C::F32) {
+            // block 4 h + e, row m <-> column 64 h + 4 m + e
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int h = 0; h < D / 64; ++h)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[4 * h + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                vo[t * NVO + i * (D / 64) + h][e], p[4 * t + i], acc[4 * h + e], 0, 0, 0);
+        } else {
+            const u32x4 pw = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
+                              pack_bf16(p[6], p[7])};
+            const bf16x8 pbv = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb)
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vo[cb], pbv, acc[cb], 0, 0, 0);
+        }
+    };
+
+    // Stores this lane's share of output row `row` (d floats, or d elements
+    // of the cache type) scaled by inv: head n's columns as the O^T blocks
+    // hold them.
+    auto store_row = [&](auto *row, float inv) {
+        using E = typename std::remove_pointer<decltype(row)>::type;
+        if constexpr (C::F32) {
+            // block 4 h + e, element i <-> column 64 h + 16 g + 4 i + e
+#pragma unroll
+            for (int h = 0; h < D / 64; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4 v = {acc[4 * h][i] * inv, acc[4 * h + 1][i] * inv, acc[4 * h + 2][i] * inv,
+                                     acc[4 * h + 3][i] * inv};
+                    *reinterpret_cast<f32x4 *>(row + 64 * h + 16 * g + 4 * i) = v;
+                }
+        } else {
+            // block cb, element i <-> column 16 cb + 4 g + i
+#pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb) {
+                if constexpr (sizeof(E) == 4)
+                    *reinterpret_cast<f32x4 *>(row + 16 * cb + 4 * g) = acc[cb] * inv;
+                else
+                    *reinterpret_cast<bf16x4 *>(row + 16 * cb + 4 * g) = __builtin_convertvector(acc[cb] * inv, bf16x4);
+            }
+        }
+    };
+
+    auto compute = [&](const int st) {
+        const int cnt = m_cnt[st];
+        Op qo[NKO], ko[2][NKO], vo[NV];
+        read_ops(stage(st), qo, ko, vo);
+        // scores: lane holds head n, keys 16 t + 4 g + r
+        float x[8];
+        scores(qo, ko, x);
         if (cnt < CK) {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -537,11 +650,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
             }
         }
         l_run += psum;
-        const u32x4 pw = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
-                          pack_bf16(p[6], p[7])};
-        const bf16x8 pbv = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-        for (int cb = 0; cb < C::CB; ++cb) acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[cb], pbv, acc[cb], 0, 0, 0);
+        pv(vo, p);
 
         if (m_last[st]) {
             // end of this range's piece of the segment
@@ -553,10 +662,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
             if (m_w0[st] == m_w1[st]) {
                 // the whole segment lies in this range: the final result
                 if (n < gblk) {
-                    __bf16 *dst = O + ((size_t)m_head0[st] + n) * D + 4 * g;
-#pragma unroll
-                    for (int cb = 0; cb < C::CB; ++cb)
-                        *reinterpret_cast<bf16x4 *>(dst + 16 * cb) = __builtin_convertvector(acc[cb] * inv, bf16x4);
+                    store_row(O + ((size_t)m_head0[st] + n) * D, inv);
                     if (LSE && g == 0) LSE[m_head0[st] + n] = lse_piece;
                 }
             } else {
@@ -564,9 +670,7 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
                 // (segment + workgroup), merged by the merge kernel
                 const size_t slot = (size_t)seg + w;
                 if (n < gblk) {
-                    float *dst = ws_o + (slot * GB + n) * D + 4 * g;
-#pragma unroll
-                    for (int cb = 0; cb < C::CB; ++cb) *reinterpret_cast<f32x4 *>(dst + 16 * cb) = acc[cb] * inv;
+                    store_row(ws_o + (slot * GB + n) * D, inv);
                     if (g == 0) ws_lse[slot * GB + n] = lse_piece;
                 }
             }
@@ -613,10 +717,10 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
 // Merges the partial results of every segment that several ranges share
 // (segments inside one range were written directly by the split kernel,
 // empty sequences too).  One single-wave workgroup per segment.
-template <int D>
+template <typename ET, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(
     const float *__restrict__ ws_o, const float *__restrict__ ws_lse, const int32_t *__restrict__ seq_lens,
-    __bf16 *__restrict__ O, float *__restrict__ LSE, int B, int Hq, int Hkv, int Lmax, int nhb, int n_wg)
+    ET *__restrict__ O, float *__restrict__ LSE, int B, int Hq, int Hkv, int Lmax, int nhb, int n_wg)
 {
     const int seg = blockIdx.x, lane = threadIdx.x;
     const int G = Hq / Hkv;
@@ -642,10 +746,11 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
     if (w0 == w1) return;
     const int hk = sub / nhb, hb = sub - hk * nhb;
     const int gblk = G - 16 * hb < 16 ? G - 16 * hb : 16;
-    merge_segment<D>(ws_o, ws_lse, O, LSE, seg, w0, w1, (size_t)b * Hq + hk * G + 16 * hb, gblk, GB, T, n_wg, lane);
+    merge_segment<ET, D>(ws_o, ws_lse, O, LSE, seg, w0, w1, (size_t)b * Hq + hk * G + 16 * hb, gblk, GB, T, n_wg,
+                         lane);
 }
 
-template <int D, int QR, int NST>
+template <typename ET, int D, int QR, int NST>
 hipError_t launch_cfg(const DecodeArgs &a, hipStream_t stream) {
     int n_wg = a.n_wg;
     if (n_wg <= 0) {
@@ -665,7 +770,7 @@ hipError_t launch_cfg(const DecodeArgs &a, hipStream_t stream) {
         if (cus == 0 || per_cu == 0) {
             hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
             if (e != hipSuccess) return e;
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_chunk_kernel<D, QR, NST>, 64, 0);
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_chunk_kernel<ET, D, QR, NST>, 64, 0);
             if (e != hipSuccess) return e;
             cus = cus > 0 ? cus : 1;
             per_cu = per_cu > 0 ? per_cu : 1;
@@ -676,21 +781,24 @@ hipError_t launch_cfg(const DecodeArgs &a, hipStream_t stream) {
     }
     if (n_wg > a.max_wg) n_wg = a.max_wg;
     const float sl2 = a.scale * LOG2E;
-    hipLaunchKernelGGL((decode_chunk_kernel<D, QR, NST>), dim3(n_wg), dim3(64), 0, stream,
-                       (const __bf16 *)a.q, (const __bf16 *)a.k_cache, (const __bf16 *)a.v_cache, a.seq_lens,
-                       (__bf16 *)a.o, a.lse, a.ws_o, a.ws_lse, a.B, a.Hq, a.Hkv, a.Lmax, a.nhb, n_wg, sl2,
-                       a.block_table, a.block_size, a.max_blocks, a.num_blocks);
+    hipLaunchKernelGGL((decode_chunk_kernel<ET, D, QR, NST>), dim3(n_wg), dim3(64), 0, stream, (const ET *)a.q,
+                       (const ET *)a.k_cache, (const ET *)a.v_cache, a.seq_lens, (ET *)a.o, a.lse, a.ws_o, a.ws_lse,
+                       a.B, a.Hq, a.Hkv, a.Lmax, a.nhb, n_wg, sl2, a.block_table, a.block_size, a.max_blocks,
+                       a.num_blocks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.B * a.Hkv * a.nhb), dim3(64), 0, stream, a.ws_o, a.ws_lse,
-                       a.seq_lens, (__bf16 *)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Lmax, a.nhb, n_wg);
+    hipLaunchKernelGGL((decode_merge_kernel<ET, D>), dim3(a.B * a.Hkv * a.nhb), dim3(64), 0, stream, a.ws_o,
+                       a.ws_lse, a.seq_lens, (ET *)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Lmax, a.nhb, n_wg);
     return hipGetLastError();
 }
 
-template <int D>
+template <typename ET, int D>
 hipError_t launch_d(const DecodeArgs &a, hipStream_t stream) {
+    // fp32 stages are twice the size: a ring of two keeps two workgroups per
+    // CU in LDS
+    constexpr int NST = sizeof(ET) == 4 ? 2 : DECODE_STAGES;
     const int G = a.Hq / a.Hkv;
-    return G <= 4 ? launch_cfg<D, 4, DECODE_STAGES>(a, stream) : launch_cfg<D, 16, DECODE_STAGES>(a, stream);
+    return G <= 4 ? launch_cfg<ET, D, 4, NST>(a, stream) : launch_cfg<ET, D, 16, NST>(a, stream);
 }
 
 }  // namespace
@@ -718,9 +826,10 @@ hipError_t decode_scratch(void **out) {
     return hipSuccess;
 }
 
-hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     if (a.B == 0) return hipSuccess;
-    return a.d == 128 ? launch_d<128>(a, stream) : launch_d<64>(a, stream);
+    if (a.f32) return a.d == 128 ? launch_d<float, 128>(a, stream) : launch_d<float, 64>(a, stream);
+    return a.d == 128 ? launch_d<__bf16, 128>(a, stream) : launch_d<__bf16, 64>(a, stream);
 }
 
 }  // namespace attn

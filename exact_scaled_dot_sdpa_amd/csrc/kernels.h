@@ -32,6 +32,7 @@ struct DecodeArgs {
     // [num_blocks, Hkv, block_size, d], Lmax = max_blocks * block_size
     const int32_t *block_table;  // [B, max_blocks]
     int block_size, max_blocks, num_blocks;
+    int f32;  // q, the caches and o are fp32 (else bf16)
 };
 
 struct Fp8FwdArgs {
@@ -57,7 +58,7 @@ struct BwdArgs {
 hipError_t launch_prefill_bf16(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_prefill_f32(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_prefill_fp8(const Fp8FwdArgs &a, hipStream_t stream);
-hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream);
 
 // Compute units of the current device (queried once per device, cached).

@@ -210,8 +210,9 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_seq_len,
  * the partial results of blocks that several ranges share are merged through
  * their log-sum-exps ("从注意力到 IO 感知执行", sec. 8, eqs. (1)-(2), applied
  * to whole ranges).  A sequence with seq_lens[b] == 0 gets O = 0 and
- * LSE = -inf.  Only dtype ATTN_BF16 is implemented (ATTN_F32 returns
- * ATTN_ERR_UNSUPPORTED); any Hq / Hkv is supported.
+ * LSE = -inf.  dtype is ATTN_BF16 (the weights enter P V rounded to bf16)
+ * or ATTN_F32 (fp32 products and weights throughout); accumulation is fp32
+ * in both cases.  Any Hq / Hkv is supported.
  *
  * Sizes: B, Hq, Hkv, max_seq_len >= 1, Hq % Hkv == 0, d in {64, 128},
  * B * Hkv * max_seq_len < 2^31.

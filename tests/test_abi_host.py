@@ -134,7 +134,7 @@ DEC_CASES = [
     (dict(B=-1), E.ATTN_ERR_INVALID_ARG),
     (dict(Lmax=-1), E.ATTN_ERR_INVALID_ARG),
     (dict(scale=float("nan")), E.ATTN_ERR_INVALID_ARG),
-    (dict(dtype=0), E.ATTN_ERR_UNSUPPORTED),            # fp32 decode not implemented
+    (dict(dtype=2), E.ATTN_ERR_INVALID_ARG),            # not an attn_dtype_t value
     (dict(d=96), E.ATTN_ERR_UNSUPPORTED),
     (dict(sl=None), E.ATTN_ERR_INVALID_ARG),
     (dict(sl=P + 2), E.ATTN_ERR_INVALID_ARG),
@@ -211,7 +211,7 @@ PDEC_CASES = [
     (dict(mb=1 << 20, bs=1 << 12), E.ATTN_ERR_UNSUPPORTED),     # max_blocks * block_size >= 2^31
     (dict(nb=1 << 20, bs=1 << 10), E.ATTN_ERR_UNSUPPORTED),     # pool rows >= 2^31
     (dict(Hq=6, Hkv=4), E.ATTN_ERR_INVALID_ARG),
-    (dict(dtype=0), E.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=2), E.ATTN_ERR_INVALID_ARG),
     (dict(d=96), E.ATTN_ERR_UNSUPPORTED),
     (dict(kp=None), E.ATTN_ERR_INVALID_ARG),
     (dict(ws=None), E.ATTN_ERR_WORKSPACE),
@@ -322,7 +322,7 @@ NOALLOC_CASES = [
     (dict(B=0), E.ATTN_ERR_INVALID_ARG),
     (dict(Lmax=0), E.ATTN_ERR_INVALID_ARG),
     (dict(scale=float("nan")), E.ATTN_ERR_INVALID_ARG),
-    (dict(dtype=0), E.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=2), E.ATTN_ERR_INVALID_ARG),
     (dict(d=96), E.ATTN_ERR_UNSUPPORTED),
     (dict(sl=None), E.ATTN_ERR_INVALID_ARG),
     (dict(o=P + 2), E.ATTN_ERR_INVALID_ARG),
