@@ -123,7 +123,7 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const v
     if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
     if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
     if (causal && Nq > Nk) return ATTN_ERR_INVALID_ARG;
-    if (!supported_d(d) || dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (!supported_d(d)) return ATTN_ERR_UNSUPPORTED;
     if ((long long)B * Hq * Nq > 0x7fffffffLL || (long long)B * Hkv * Nk > 0x7fffffffLL)
         return ATTN_ERR_UNSUPPORTED;
     // every tensor the kernels touch must be present and aligned (q and do
@@ -137,7 +137,7 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const v
 
     attn::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, (float *)workspace, B, Hq, Hkv, Nq, Nk, d, scale,
                     causal ? 1 : 0};
-    const hipError_t e = attn::launch_bwd_bf16(a, stream);
+    const hipError_t e = dtype == ATTN_F32 ? attn::launch_bwd_f32(a, stream) : attn::launch_bwd_bf16(a, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

@@ -48,7 +48,7 @@ struct BwdArgs {
     const void *q, *k, *v, *o, *dout;
     const float *lse;
     void *dq, *dk, *dv;
-    float *ws_d;  // [2, B*Hq*Nq] fp32: do_i . o_i, then lse_i * log2(e), per row
+    float *ws_d;  // [2, B*Hq*Nq] fp32: do_i . o_i, then lse_i * log2(e), per row (fp32: the first half only)
     int B, Hq, Hkv, Nq, Nk, d;
     float scale;
     int causal;
@@ -60,6 +60,7 @@ hipError_t launch_prefill_f32(const FwdArgs &a, hipStream_t stream);
 hipError_t launch_prefill_fp8(const Fp8FwdArgs &a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs &a, hipStream_t stream);
+hipError_t launch_bwd_f32(const BwdArgs &a, hipStream_t stream);
 
 // Compute units of the current device (queried once per device, cached).
 hipError_t device_cu_count(int *out);

@@ -156,11 +156,12 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Nq);
  *              device memory, 16-byte aligned; contents on entry do not
  *              matter; calls that overlap in time must not share it.
  *
- * Sizes, head mapping, scale and causal alignment as attn_fwd.  Only
- * dtype == ATTN_BF16 is implemented (ATTN_F32 returns ATTN_ERR_UNSUPPORTED);
- * products take bf16 operands (the weights and ds rounded to nearest even)
- * with fp32 accumulation, and the gradients are rounded to bf16.  The result
- * is deterministic (no atomics).
+ * Sizes, head mapping, scale and causal alignment as attn_fwd.  With
+ * dtype == ATTN_BF16, products take bf16 operands (the weights and ds
+ * rounded to nearest even) with fp32 accumulation, and the gradients are
+ * rounded to bf16; with ATTN_F32 every product and sum is fp32 (for
+ * full-precision gradient checks).  The result is deterministic (no
+ * atomics).
  *
  * Returns ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED,
  * ATTN_ERR_WORKSPACE (nothing launched in these three cases) or

@@ -11,6 +11,7 @@ hipError_t launch_prefill_f32(const FwdArgs &, hipStream_t) { return hipSuccess;
 hipError_t launch_prefill_fp8(const Fp8FwdArgs &, hipStream_t) { return hipSuccess; }
 hipError_t launch_decode(const DecodeArgs &, hipStream_t) { return hipSuccess; }
 hipError_t launch_bwd_bf16(const BwdArgs &, hipStream_t) { return hipSuccess; }
+hipError_t launch_bwd_f32(const BwdArgs &, hipStream_t) { return hipSuccess; }
 hipError_t device_cu_count(int *out) {
     *out = 256;
     return hipSuccess;

@@ -253,7 +253,6 @@ BWD_CASES = [
     (dict(causal=1, Nq=65), E.ATTN_ERR_INVALID_ARG),
     (dict(scale=float("nan")), E.ATTN_ERR_INVALID_ARG),
     (dict(dtype=5), E.ATTN_ERR_INVALID_ARG),
-    (dict(dtype=0), E.ATTN_ERR_UNSUPPORTED),             # fp32 backward not implemented
     (dict(d=32), E.ATTN_ERR_UNSUPPORTED),
     (dict(lse=None), E.ATTN_ERR_INVALID_ARG),
     (dict(do=None), E.ATTN_ERR_INVALID_ARG),
