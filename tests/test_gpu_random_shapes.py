@@ -114,6 +114,33 @@ def test_random_decode_paged(orc, case):
     assert_close("LSE", I.to_f64(lse), lse_ref, TOL_LSE)
 
 
+@pytest.mark.parametrize("case", _decode_shapes(6, 2031), ids=lambda c: "d%d_B%d_H%d-%d_L%d_kps%d" % c)
+def test_random_decode_f32(orc, case):
+    d, B, Hq, Hkv, Lmax, kps = case
+    say("[random decode f32] %s" % (case,))
+    sl, q, kc, vc = I.decode_inputs(B, Hq, Hkv, Lmax, d, "f32", seed=5600 + B * 13 + Lmax + Hq, lo=0, hi=Lmax)
+    o, lse = gpu_decode(sl, q, kc, vc, 1.0 / np.sqrt(d), kps)
+    o_ref, lse_ref = orc.decode(I.to_f64(q), I.to_f64(kc), I.to_f64(vc), sl.numpy(), 1.0 / np.sqrt(d))
+    assert_close("O", o, o_ref, TOL_O["f32"])
+    assert_close("LSE", lse, lse_ref, TOL_LSE)
+
+
+@pytest.mark.parametrize("case", _decode_shapes(4, 2032), ids=lambda c: "d%d_B%d_H%d-%d_L%d_kps%d" % c)
+def test_random_decode_paged_f32(orc, case):
+    d, B, Hq, Hkv, Lmax, kps = case
+    bs = int(np.random.default_rng(Lmax + B + 1).choice([1, 8, 16, 32, 64, 100]))
+    say("[random paged f32] %s bs=%d" % (case, bs))
+    sl, q, kp, vp, bt = I.paged_decode_inputs(B, Hq, Hkv, d, bs, -(-Lmax // bs), "f32", seed=5700 + B + Lmax,
+                                              lo=0, hi=Lmax, spare_blocks=1)
+    o, lse = E.attn_decode_paged(dev(q), dev(kp), dev(vp), dev(bt), dev(sl), scale=1.0 / np.sqrt(d),
+                                 keys_per_split=kps)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = orc.decode_paged(I.to_f64(q), I.to_f64(kp), I.to_f64(vp), bt.numpy(), sl.numpy(),
+                                      1.0 / np.sqrt(d))
+    assert_close("O", I.to_f64(o), o_ref, TOL_O["f32"])
+    assert_close("LSE", I.to_f64(lse), lse_ref, TOL_LSE)
+
+
 @pytest.mark.parametrize("case", _prefill_shapes(10, 2029, max_len=383), ids=_ids)
 def test_random_bwd(orc, case):
     """Gradients against the oracle's, relative to each tensor's largest
