@@ -1,0 +1,36 @@
+"""include/attn.h used from C and from C++ (CPU only).
+
+tests/c_abi/header_use.c is built against the header alone, with gcc as C99
+and with g++ as C++11, both under -Wall -Wextra -Werror -pedantic, and
+linked to the built libattn.so.  The program assigns every entry point to a
+function pointer of its documented type (so a changed prototype fails to
+build), checks the enum values, the status names and the workspace queries,
+and calls each compute entry point with null tensors, which every one must
+refuse with ATTN_ERR_INVALID_ARG before any HIP call."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import exact_scaled_dot_sdpa_amd as E
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "tests", "c_abi", "header_use.c")
+INC = os.path.join(ROOT, "include")
+
+COMPILERS = [("gcc", ["-std=c99", "-x", "c"]), ("g++", ["-std=c++11", "-x", "c++"])]
+
+
+@pytest.mark.parametrize("cc,lang", COMPILERS, ids=["c99", "c++11"])
+def test_header_builds_links_and_runs(tmp_path, cc, lang):
+    if shutil.which(cc) is None:
+        pytest.skip("needs %s" % cc)
+    libdir = os.path.dirname(E.lib_path())
+    exe = str(tmp_path / "header_use")
+    cmd = [cc, *lang, "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", INC, SRC, "-x", "none", "-L", libdir,
+           "-lattn", "-Wl,-rpath," + libdir, "-o", exe]
+    b = subprocess.run(cmd, capture_output=True, text=True)
+    assert b.returncode == 0, b.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
