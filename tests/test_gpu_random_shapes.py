@@ -166,3 +166,25 @@ def test_random_bwd(orc, case):
         say("  %s max err %.2e of max|ref|, rms err %.2e of rms" % (name, e_max / max(top, 1e-300),
                                                                    e_rms / max(rms, 1e-300)))
         assert e_max <= 2e-2 * top + floor and e_rms <= 6e-3 * rms + floor, name
+
+
+@pytest.mark.parametrize("case", _prefill_shapes(6, 2039, max_len=200), ids=_ids)
+def test_random_bwd_f32(orc, case):
+    """fp32 gradients against the oracle's, at the fp32 backward test's
+    bound: max |g - ref| <= 3e-5 * max|ref| + 2e-6 per tensor."""
+    d, B, Hq, Hkv, Nq, Nk, causal, scale = case
+    say("[random bwd f32] %s" % (case,))
+    q, k, v, do = I.bwd_inputs(B, Hq, Hkv, Nq, Nk, d, "f32", seed=5600 + Nq * 7 + Nk + Hq)
+    qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
+    o, lse = E.attn_fwd(qd, kd, vd, scale=scale, causal=causal)
+    grads = E.attn_bwd(qd, kd, vd, o, dod, lse, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    refs = orc.attn_bwd(I.to_f64(q), I.to_f64(k), I.to_f64(v), I.to_f64(do), scale, causal)
+    for name, g, r in zip(("dq", "dk", "dv"), grads, refs):
+        assert g.dtype == torch.float32, name
+        g = I.to_f64(g)
+        assert np.isfinite(g).all(), name
+        top = float(np.abs(r).max())
+        e_max = float(np.abs(g - r).max())
+        say("  %s max err %.2e (max|ref| %.2e)" % (name, e_max, top))
+        assert e_max <= 3e-5 * top + 2e-6, name
