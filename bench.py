@@ -17,7 +17,11 @@ The JSON line reports the prefill throughput in TFLOP/s as `value` (algorithmic
 FLOPs: 4*d per visible query/key pair), the decode bandwidth in GB/s (valid
 cache rows plus q, o, lse) in `decode`, and for each kernel its roofline
 fraction from its average duration measured with HIP events on the stream the
-kernels run on (mean, with the median beside it).  `cpu_baseline` times the
+kernels run on (mean, with the median beside it).  The prefill roofline also
+gives the engine clock that the committed SQ counter run observed over the
+kernel (`sclk_ghz_counters`) and the same rate against the dense peak scaled
+to that clock (`frac_at_sclk`); `frac` stays against the published peak.
+`cpu_baseline` times the
 fp64 oracle on a bounded sample of the prefill rows on the host cores, and
 (`per_config`) on each smaller prefill workload in full, next to that
 workload's GPU time; `parity` compares the timed prefill's outputs with the
@@ -56,6 +60,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (published)
+PEAK_SCLK_GHZ = 2.4         # the engine clock the published MFMA peaks assume
 METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak (prefill); KV-cache GB/s & % HBM (decode)"
 N_REPLICAS = 4
 
@@ -558,13 +563,16 @@ def main():
     }
     if run_p:
         tr = stored_traffic("prefill")
+        clk = stored_clock("prefill")
         out["roofline"] = {
             "bound": "mfma", "achieved": round(p_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4), "traffic": tr,
             "kernel": "prefill_bf16_kernel<128,true,8,8>", "avg_launch_ms": round(p_ms, 5),
             "median_launch_ms": round(p_med, 5),
             "median_tflops": round(p_flops / (p_med * 1e-3) / 1e12, 2),
-            "sclk_ghz_counters": stored_clock("prefill"),
+            "sclk_ghz_counters": clk,
+            # the same rate against the dense peak scaled to that observed clock
+            "frac_at_sclk": round(p_tflops / (PEAK_BF16_TFLOPS * clk / PEAK_SCLK_GHZ), 4) if clk else None,
         }
     if run_d:
         tr = stored_traffic("decode")
