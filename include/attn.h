@@ -77,7 +77,9 @@ typedef enum {
  *
  * Query head h uses K/V head h / (Hq / Hkv) (contiguous groups).
  * scale multiplies q.k before masking and the softmax (1/sqrt(d) in the
- * usual case; any finite value is accepted).
+ * usual case; any finite value is accepted).  The kernels form q.k and
+ * scale * log2(e) * q.k in fp32, so the results hold while those stay finite
+ * (|scale * q.k| below about 2.3e38); beyond that rows may read NaN.
  * causal != 0 masks key j for query row i when j > i + (Nk - Nq): the query
  * block is aligned with the END of the key sequence, so the last query row
  * sees every key (chunked prefill and decode agree with full causal prefill).
