@@ -47,8 +47,13 @@
 extern "C" {
 #endif
 
-/* The HIP stream handle type (same declaration as hip_runtime_api.h). */
+/* The HIP stream handle type, declared as hip_runtime_api.h declares it.
+ * Skipped when that header came first: C99 forbids repeating a typedef (C11
+ * and C++ accept it, so there either include order works; in C99 include
+ * hip_runtime_api.h first, or this header alone). */
+#ifndef HIP_INCLUDE_HIP_HIP_RUNTIME_API_H
 typedef struct ihipStream_t *hipStream_t;
+#endif
 
 /* Element type of q, k, v, o (and of the caches for decode). */
 typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;

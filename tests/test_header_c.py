@@ -2,7 +2,8 @@
 
 tests/c_abi/header_use.c is built against the header alone, with gcc as C99
 and with g++ as C++11, both under -Wall -Wextra -Werror -pedantic, and
-linked to the built libattn.so.  The program assigns every entry point to a
+linked to the built libattn.so; then once more each way with HIP's runtime API
+header included first, which declares the same stream type.  The program assigns every entry point to a
 function pointer of its documented type (so a changed prototype fails to
 build), checks the enum values, the status names and the workspace queries,
 and calls each compute entry point with null tensors, which every one must
@@ -19,13 +20,22 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "tests", "c_abi", "header_use.c")
 INC = os.path.join(ROOT, "include")
 
-COMPILERS = [("gcc", ["-std=c99", "-x", "c"]), ("g++", ["-std=c++11", "-x", "c++"])]
+HIP_API = "/opt/rocm/include/hip/hip_runtime_api.h"
+# the same program with HIP's runtime API header included before attn.h
+# (-include), as a program that also calls HIP itself would; HIP's headers are
+# system headers here, so only attn.h's own warnings count
+WITH_HIP = ["-isystem", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__", "-include", "hip/hip_runtime_api.h"]
+
+COMPILERS = [("gcc", ["-std=c99", "-x", "c"]), ("g++", ["-std=c++11", "-x", "c++"]),
+             ("gcc", ["-std=c99", *WITH_HIP, "-x", "c"]), ("g++", ["-std=c++11", *WITH_HIP, "-x", "c++"])]
 
 
-@pytest.mark.parametrize("cc,lang", COMPILERS, ids=["c99", "c++11"])
+@pytest.mark.parametrize("cc,lang", COMPILERS, ids=["c99", "c++11", "c99-after-hip", "c++11-after-hip"])
 def test_header_builds_links_and_runs(tmp_path, cc, lang):
     if shutil.which(cc) is None:
         pytest.skip("needs %s" % cc)
+    if "-include" in lang and not os.path.exists(HIP_API):
+        pytest.skip("needs %s" % HIP_API)
     libdir = os.path.dirname(E.lib_path())
     exe = str(tmp_path / "header_use")
     cmd = [cc, *lang, "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", INC, SRC, "-x", "none", "-L", libdir,
