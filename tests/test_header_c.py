@@ -9,6 +9,7 @@ build), checks the enum values, the status names and the workspace queries,
 and calls each compute entry point with null tensors, which every one must
 refuse with ATTN_ERR_INVALID_ARG before any HIP call."""
 import os
+import re
 import shutil
 import subprocess
 
@@ -44,3 +45,19 @@ def test_header_builds_links_and_runs(tmp_path, cc, lang):
     assert b.returncode == 0, b.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
+
+
+def test_readme_c_example_compiles(tmp_path):
+    """The C example in README.md compiles as C99 against include/attn.h and
+    HIP's runtime API header (compile only: it needs a GPU to run)."""
+    if shutil.which("gcc") is None or not os.path.exists(HIP_API):
+        pytest.skip("needs gcc and %s" % HIP_API)
+    text = open(os.path.join(ROOT, "README.md")).read()
+    blocks = re.findall(r"```c\n(.*?)```", text, flags=re.S)
+    assert len(blocks) == 1, "README.md should hold exactly one C example"
+    src = tmp_path / "readme_example.c"
+    src.write_text(blocks[0])
+    b = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-isystem", "/opt/rocm/include",
+                        "-D__HIP_PLATFORM_AMD__", "-I", INC, "-c", str(src), "-o", str(tmp_path / "ex.o")],
+                       capture_output=True, text=True)
+    assert b.returncode == 0, b.stderr
