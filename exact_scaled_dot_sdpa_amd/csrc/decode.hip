@@ -803,29 +803,6 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-// Scratch for attn_decode_noalloc: the split kernels' partial results live
-// here instead of in a caller-provided workspace.  Each device holds its own
-// copy until the process ends.  In host code `scratch` is only a stand-in
-// for the symbol; its device address comes from hipGetSymbolAddress.
-static __device__ __align__(256) char scratch[DECODE_SCRATCH_BYTES];
-
-hipError_t decode_scratch(void **out) {
-    static std::atomic<void *> addr[64];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    void *p = addr[dev].load(std::memory_order_acquire);
-    if (p == nullptr) {
-        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-        if (e != hipSuccess) return e;
-        if (p == nullptr) return hipErrorInvalidSymbol;
-        addr[dev].store(p, std::memory_order_release);  // concurrent first calls store the same address
-    }
-    *out = p;
-    return hipSuccess;
-}
-
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     if (a.B == 0) return hipSuccess;
     if (a.f32) return a.d == 128 ? launch_d<float, 128>(a, stream) : launch_d<float, 64>(a, stream);
