@@ -50,13 +50,16 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int max_seq_len, int keys_per_spl
     return p;
 }
 
-// fp32 partial outputs [slots, gb, d], then (256-byte aligned) partial LSEs [slots, gb]
-void workspace_layout(const DecodePlan &p, int d, size_t *o_bytes, size_t *total) {
+// fp32 partial outputs [slots, gb, d], then (256-byte aligned) partial LSEs
+// [slots, gb], then (256-byte aligned) int32 per-range records [max_wg, 4]
+void workspace_layout(const DecodePlan &p, int d, size_t *o_bytes, size_t *rec_off, size_t *total) {
     const size_t rows = (size_t)p.slots * p.gb;
     size_t ob = rows * (size_t)d * sizeof(float);
     ob = (ob + 255) & ~(size_t)255;
     *o_bytes = ob;
-    *total = ob + rows * sizeof(float);
+    const size_t ro = (ob + rows * sizeof(float) + 255) & ~(size_t)255;
+    *rec_off = ro;
+    *total = ro + (size_t)p.max_wg * 4 * sizeof(int32_t);
 }
 
 // Every size is at least 1 and query heads form whole groups.
@@ -144,8 +147,8 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const v
 size_t attn_decode_split_workspace_bytes(int B, int Hq, int Hkv, int max_seq_len, int d, int keys_per_split)
 {
     if (!decode_sizes_ok(B, Hq, Hkv, max_seq_len) || !supported_d(d) || keys_per_split < 0) return 0;
-    size_t ob, total;
-    workspace_layout(decode_plan(B, Hq, Hkv, max_seq_len, keys_per_split), d, &ob, &total);
+    size_t ob, ro, total;
+    workspace_layout(decode_plan(B, Hq, Hkv, max_seq_len, keys_per_split), d, &ob, &ro, &total);
     return total;
 }
 
@@ -185,8 +188,8 @@ int decode_call(const void *q, const void *k_cache, const void *v_cache, const i
     if (rows > 0x7fffffffLL || page_keys > 0x7fffffffLL || (long long)B * Hq > 0x7fffffffLL ||
         p.slots > 0x7fffffffLL)
         return ATTN_ERR_UNSUPPORTED;
-    size_t ob, need;
-    workspace_layout(p, d, &ob, &need);
+    size_t ob, ro, need;
+    workspace_layout(p, d, &ob, &ro, &need);
     if (use_scratch) {
         if (need > attn::DECODE_SCRATCH_BYTES) return ATTN_ERR_WORKSPACE;
         if (attn::decode_scratch(&workspace) != hipSuccess) return ATTN_ERR_LAUNCH;
@@ -196,7 +199,8 @@ int decode_call(const void *q, const void *k_cache, const void *v_cache, const i
 
     attn::DecodeArgs a{q, k_cache, v_cache, seq_lens, o, lse, B, Hq, Hkv, Lmax, d, scale,
                        p.nhb, p.n_wg, p.max_wg, (float *)workspace, (float *)((char *)workspace + ob),
-                       block_table, block_size, max_blocks, num_blocks, dtype == ATTN_F32 ? 1 : 0};
+                       (int32_t *)((char *)workspace + ro), block_table, block_size, max_blocks, num_blocks,
+                       dtype == ATTN_F32 ? 1 : 0};
     const hipError_t e = attn::launch_decode(a, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }

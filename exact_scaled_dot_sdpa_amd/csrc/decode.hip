@@ -78,6 +78,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -147,6 +148,25 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
         if (lane >= o) x += y;
     }
     return x;
+}
+
+// Sum of x over the wave (every lane gets it).
+__device__ __forceinline__ int wave_total(int x, int lane) {
+    return __builtin_amdgcn_readlane(wave_incl_scan(x, lane), 63);
+}
+
+// Lengths of the 8 pages of 64 sequences from p8 (lane i: sequence
+// p8 + 64 k + i in Lg[k]; 0 past the batch), all loads issued before any is
+// used, so the 8 pages cost one memory round trip.
+__device__ __forceinline__ void load_pages8(int (&Lg)[8], const int32_t *__restrict__ seq_lens, int p8, int B,
+                                            int Lmax, int lane) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const long long idx = (long long)p8 + 64 * k + lane;
+        Lg[k] = idx < B ? seq_lens[idx] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) Lg[k] = clamp_len(Lg[k], Lmax);
 }
 
 // Round-to-nearest-even pair conversion fp32 -> packed bf16 (lo in bits 0..15).
@@ -281,9 +301,9 @@ __device__ void merge_segment(const float *ws_o, const float *ws_lse, OT *O, flo
 template <typename ET, int D, int QR, int NST>
 __global__ __launch_bounds__(64) void decode_chunk_kernel(
     const ET *__restrict__ Q, const ET *__restrict__ Kc, const ET *__restrict__ Vc, const int32_t *__restrict__ seq_lens,
-    ET *__restrict__ O, float *__restrict__ LSE, float *__restrict__ ws_o, float *__restrict__ ws_lse, int B, int Hq,
-    int Hkv, int Lmax, int nhb, int n_wg, float sl2, const int32_t *__restrict__ block_table, int bs,
-    int max_blocks, int num_blocks)
+    ET *__restrict__ O, float *__restrict__ LSE, float *__restrict__ ws_o, float *__restrict__ ws_lse,
+    int32_t *__restrict__ ws_rec, int B, int Hq, int Hkv, int Lmax, int nhb, int n_wg, float sl2,
+    const int32_t *__restrict__ block_table, int bs, int max_blocks, int num_blocks)
 {
     using C = DC<ET, D>;
     using S = Stage<ET, D, QR>;
@@ -304,23 +324,39 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
     // ---- this workgroup's key range [a0, a1) -----------------------------
     // The first page of 64 sequence lengths serves both the total and the
     // search, so a batch of up to 64 sequences costs one memory round trip.
+    // Larger batches load the other pages eight at a time (one round trip
+    // per 512 sequences), for the total and again, up to the page that holds
+    // the range's first key, for the search.  A page's sum fits in 32 bits
+    // (the boundary bounds 64 * max_seq_len); the batch's sum is 64-bit.
     int pageL = lane < B ? clamp_len(seq_lens[lane], Lmax) : 0;
     int incl = wave_incl_scan(pageL, lane);
     long long T = __builtin_amdgcn_readlane(incl, 63);
-    for (int p2 = 64; p2 < B; p2 += 64) {
-        const int L = p2 + lane < B ? clamp_len(seq_lens[p2 + lane], Lmax) : 0;
-        T += __builtin_amdgcn_readlane(wave_incl_scan(L, lane), 63);
+    for (int p8 = 64; p8 < B; p8 += 512) {
+        int Lg[8];
+        load_pages8(Lg, seq_lens, p8, B, Lmax, lane);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) T += wave_total(Lg[k], lane);
     }
     T *= nsub;
+    // this range's record for the merge kernel: no shared segment ends in it
+    // (rewritten below by the range that holds a shared segment's last piece)
+    if (lane == 0) *reinterpret_cast<i32x4 *>(ws_rec + 4 * w) = i32x4{-1, 0, 0, 0};
     // sequences with no visible key (seq_len 0) get O = 0 and LSE = -inf from
-    // workgroup b mod n_wg; no range ever reaches them
-    for (int bz = w; bz < B; bz += n_wg) {
-        const int L = bz < 64 ? __builtin_amdgcn_readlane(pageL, bz) : clamp_len(seq_lens[bz], Lmax);
-        if (L == 0) {
-            char *dst = reinterpret_cast<char *>(O + (size_t)bz * Hq * D);
+    // workgroup b mod n_wg (no range ever reaches them); lane i checks
+    // sequence w + i n_wg, so one pass covers 64 of this workgroup's
+    for (long long base = w; base < B; base += 64LL * n_wg) {
+        const long long bz = base + (long long)lane * n_wg;
+        const int from_page = __shfl(pageL, (int)(bz & 63), 64);
+        int L = 1;
+        if (bz < B) L = bz < 64 ? from_page : clamp_len(seq_lens[bz], Lmax);
+        unsigned long long zero = __builtin_amdgcn_ballot_w64(L == 0);
+        while (zero) {
+            const long long bzz = base + (long long)__builtin_ctzll(zero) * n_wg;
+            zero &= zero - 1;
+            char *dst = reinterpret_cast<char *>(O + (size_t)bzz * Hq * D);
             for (int i = lane; i < Hq * C::ROWB / 16; i += 64) *reinterpret_cast<u32x4 *>(dst + 16 * i) = u32x4{};
             if (LSE)
-                for (int i = lane; i < Hq; i += 64) LSE[(size_t)bz * Hq + i] = -INFINITY;
+                for (int i = lane; i < Hq; i += 64) LSE[(size_t)bzz * Hq + i] = -INFINITY;
         }
     }
     const long long a0 = range_start(w, T, n_wg), a1 = range_start(w + 1, T, n_wg);
@@ -330,18 +366,37 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
     // position of sequence b's first key in the batch list
     int pb = 0, f = 0;
     long long bstart = 0;
-    for (;;) {  // a0 < T, so some page holds it
-        const long long end_i = bstart + (long long)incl * nsub;
-        const unsigned long long hit = __builtin_amdgcn_ballot_w64(end_i > a0);
-        if (hit) {
-            f = __builtin_ctzll(hit);
-            bstart += (long long)(__builtin_amdgcn_readlane(incl, f) - __builtin_amdgcn_readlane(pageL, f)) * nsub;
-            break;
+    {
+        unsigned long long hit = __builtin_amdgcn_ballot_w64((long long)incl * nsub > a0);
+        if (!hit) {
+            bstart = (long long)__builtin_amdgcn_readlane(incl, 63) * nsub;
+            bool found = false;
+            for (int p8 = 64; p8 < B && !found; p8 += 512) {
+                int Lg[8];
+                load_pages8(Lg, seq_lens, p8, B, Lmax, lane);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    if (!found) {  // uniform
+                        const long long tot = (long long)wave_total(Lg[k], lane) * nsub;
+                        if (bstart + tot > a0) {
+                            found = true;
+                            pb = p8 + 64 * k;
+                            pageL = Lg[k];
+                        } else {
+                            bstart += tot;
+                        }
+                    }
+                }
+            }
+            // a0 < T, so some page holds it; lengths that changed between the
+            // two reads (a caller's race) end the walk instead of running on
+            if (!found) return;
+            incl = wave_incl_scan(pageL, lane);
+            hit = __builtin_amdgcn_ballot_w64(bstart + (long long)incl * nsub > a0);
+            if (!hit) return;
         }
-        bstart += (long long)__builtin_amdgcn_readlane(incl, 63) * nsub;
-        pb += 64;
-        pageL = pb + lane < B ? clamp_len(seq_lens[pb + lane], Lmax) : 0;
-        incl = wave_incl_scan(pageL, lane);
+        f = __builtin_ctzll(hit);
+        bstart += (long long)(__builtin_amdgcn_readlane(incl, f) - __builtin_amdgcn_readlane(pageL, f)) * nsub;
     }
     int b = pb + f;
     int Lb = __builtin_amdgcn_readlane(pageL, f);
@@ -673,6 +728,10 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
                     store_row(ws_o + (slot * GB + n) * D, inv);
                     if (g == 0) ws_lse[slot * GB + n] = lse_piece;
                 }
+                // the segment's last piece: record it for the merge kernel
+                if (m_w1[st] == w && lane == 0)
+                    *reinterpret_cast<i32x4 *>(ws_rec + 4 * w) =
+                        i32x4{seg, m_w0[st], (int)(unsigned)(unsigned long long)T, (int)((unsigned long long)T >> 32)};
             }
         }
     };
@@ -714,39 +773,28 @@ __global__ __launch_bounds__(64) void decode_chunk_kernel(
     }
 }
 
-// Merges the partial results of every segment that several ranges share
+// Merges the partial results of the segments that several ranges share
 // (segments inside one range were written directly by the split kernel,
-// empty sequences too).  One single-wave workgroup per segment.
+// empty sequences too).  Workgroup w (one wave) takes the segment whose last
+// piece lies in range w, as the split kernel recorded it: the segment, its
+// first range and the batch's key count, so no sequence lengths are read.
 template <typename ET, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(
-    const float *__restrict__ ws_o, const float *__restrict__ ws_lse, const int32_t *__restrict__ seq_lens,
-    ET *__restrict__ O, float *__restrict__ LSE, int B, int Hq, int Hkv, int Lmax, int nhb, int n_wg)
+    const float *__restrict__ ws_o, const float *__restrict__ ws_lse, const int32_t *__restrict__ ws_rec,
+    ET *__restrict__ O, float *__restrict__ LSE, int Hq, int Hkv, int nhb, int n_wg)
 {
-    const int seg = blockIdx.x, lane = threadIdx.x;
+    const int w = blockIdx.x, lane = threadIdx.x;
+    const i32x4 r = *reinterpret_cast<const i32x4 *>(ws_rec + 4 * w);
+    const int seg = r[0];
+    if (seg < 0) return;
+    const long long T = (long long)(((unsigned long long)(unsigned)r[3] << 32) | (unsigned)r[2]);
     const int G = Hq / Hkv;
     const int GB = G < 16 ? G : 16;
     const int nsub = Hkv * nhb;
     const int b = seg / nsub, sub = seg - b * nsub;
-    // batch total and the prefix of sequence b
-    long long T = 0, Pb = 0;
-    int Lb = 0;
-    for (int pb = 0; pb < B; pb += 64) {
-        const int L = pb + lane < B ? clamp_len(seq_lens[pb + lane], Lmax) : 0;
-        const int incl = wave_incl_scan(L, lane);
-        if (b >= pb && b < pb + 64) {
-            Lb = __builtin_amdgcn_readlane(L, b - pb);
-            Pb = T + __builtin_amdgcn_readlane(incl, b - pb) - Lb;
-        }
-        T += __builtin_amdgcn_readlane(incl, 63);
-    }
-    if (Lb == 0) return;
-    T *= nsub;
-    const long long S0 = Pb * nsub + (long long)sub * Lb, S1 = S0 + Lb;
-    const int w0 = (int)(((S0 + 1) * n_wg - 1) / T), w1 = (int)((S1 * n_wg - 1) / T);
-    if (w0 == w1) return;
     const int hk = sub / nhb, hb = sub - hk * nhb;
     const int gblk = G - 16 * hb < 16 ? G - 16 * hb : 16;
-    merge_segment<ET, D>(ws_o, ws_lse, O, LSE, seg, w0, w1, (size_t)b * Hq + hk * G + 16 * hb, gblk, GB, T, n_wg,
+    merge_segment<ET, D>(ws_o, ws_lse, O, LSE, seg, r[1], w, (size_t)b * Hq + hk * G + 16 * hb, gblk, GB, T, n_wg,
                          lane);
 }
 
@@ -783,12 +831,12 @@ hipError_t launch_cfg(const DecodeArgs &a, hipStream_t stream) {
     const float sl2 = a.scale * LOG2E;
     hipLaunchKernelGGL((decode_chunk_kernel<ET, D, QR, NST>), dim3(n_wg), dim3(64), 0, stream, (const ET *)a.q,
                        (const ET *)a.k_cache, (const ET *)a.v_cache, a.seq_lens, (ET *)a.o, a.lse, a.ws_o, a.ws_lse,
-                       a.B, a.Hq, a.Hkv, a.Lmax, a.nhb, n_wg, sl2, a.block_table, a.block_size, a.max_blocks,
-                       a.num_blocks);
+                       a.ws_rec, a.B, a.Hq, a.Hkv, a.Lmax, a.nhb, n_wg, sl2, a.block_table, a.block_size,
+                       a.max_blocks, a.num_blocks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<ET, D>), dim3(a.B * a.Hkv * a.nhb), dim3(64), 0, stream, a.ws_o,
-                       a.ws_lse, a.seq_lens, (ET *)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Lmax, a.nhb, n_wg);
+    hipLaunchKernelGGL((decode_merge_kernel<ET, D>), dim3(n_wg), dim3(64), 0, stream, a.ws_o, a.ws_lse, a.ws_rec,
+                       (ET *)a.o, a.lse, a.Hq, a.Hkv, a.nhb, n_wg);
     return hipGetLastError();
 }
 

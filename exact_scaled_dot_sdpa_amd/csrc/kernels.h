@@ -28,6 +28,8 @@ struct DecodeArgs {
     int max_wg;     // workgroups the workspace has partial-result slots for
     float *ws_o;    // [B*Hkv*nhb + max_wg - 1 slots, min(G, 16) heads, d] fp32
     float *ws_lse;  // [slots, min(G, 16)] fp32
+    int32_t *ws_rec;  // [max_wg, 4] per range: the shared segment whose last piece it holds (or -1),
+                      // that segment's first range, the batch's key count (low, high 32 bits)
     // paged cache (block_table != nullptr): k_cache / v_cache are a pool
     // [num_blocks, Hkv, block_size, d], Lmax = max_blocks * block_size
     const int32_t *block_table;  // [B, max_blocks]

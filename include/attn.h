@@ -184,9 +184,11 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o,
  * attn_decode_workspace_bytes -- bytes of device workspace attn_decode needs
  * for these sizes: fp32 partial results of the split (see attn_decode),
  *   partial outputs [S, min(G, 16), d], then (from the next 256-byte
- *   boundary) partial LSEs [S, min(G, 16)],
- * with G = Hq / Hkv and S = B * Hkv * ceil(G / 16) + 2047 slots.  Returns 0
- * for sizes attn_decode would reject.
+ *   boundary) partial LSEs [S, min(G, 16)], then (from the next 256-byte
+ *   boundary) one record of four int32 per split workgroup [W, 4], which
+ *   tells the merge which shared block ends in that workgroup's range,
+ * with G = Hq / Hkv, W = 2048 and S = B * Hkv * ceil(G / 16) + W - 1 slots.
+ * Returns 0 for sizes attn_decode would reject.
  */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int max_seq_len,
                                    int d);
@@ -241,8 +243,8 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache,
  * max_seq_len / keys_per_split) workgroups clamped to [1, 2048];
  * keys_per_split == 0 is the default of attn_decode (two workgroups per
  * compute unit) or attn_decode_paged (as many as the device holds at once).
- * The workspace then has S = B * Hkv * ceil(G / 16) + W - 1 slots (W = 2048
- * for keys_per_split == 0), laid out as for attn_decode.  Everything else is
+ * The workspace then has S = B * Hkv * ceil(G / 16) + W - 1 slots and W
+ * records (W = 2048 for keys_per_split == 0), laid out as for attn_decode.  Everything else is
  * attn_decode's.  The result is the same up to the order of floating-point
  * sums (split invariance).
  */

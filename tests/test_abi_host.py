@@ -163,7 +163,7 @@ def _ws_bytes(B, Hq, Hkv, Lmax, d, kps):
     """The workspace size the header documents: slots of min(G, 16) heads,
     one per (sequence, K/V head, block of 16 query heads) plus one per split
     workgroup beyond the first; fp32 outputs, then (256-byte aligned) fp32
-    LSEs."""
+    LSEs, then (256-byte aligned) one record of four int32 per workgroup."""
     G = Hq // Hkv
     nhb = -(-G // 16)
     gb = min(G, 16)
@@ -172,7 +172,9 @@ def _ws_bytes(B, Hq, Hkv, Lmax, d, kps):
     else:
         n_wg = 2048
     rows = (B * Hkv * nhb + n_wg - 1) * gb
-    return -(-(rows * d * 4) // 256) * 256 + rows * 4
+    ob = -(-(rows * d * 4) // 256) * 256
+    ro = -(-(ob + rows * 4) // 256) * 256
+    return ro + n_wg * 16
 
 
 def test_decode_workspace_bytes():
@@ -182,8 +184,10 @@ def test_decode_workspace_bytes():
         assert f(*args) == _ws_bytes(*args), args
     for args in [(16, 32, 8, 4096, 128), (3, 6, 2, 100, 64), (1, 1, 1, 1, 64)]:
         assert E.attn_decode_workspace_bytes(*args) == _ws_bytes(*args, 0), args
-    # 16 x 8 segments + 512 workgroups of 1024 keys - 1, four heads each
-    assert f(16, 32, 8, 4096, 128, 1024) == 639 * 4 * 128 * 4 + 639 * 4 * 4
+    # 16 x 8 segments + 512 workgroups of 1024 keys - 1, four heads each: the
+    # outputs (1308672 bytes, 256-aligned), the LSEs up to the next 256-byte
+    # boundary, then 512 records of 16 bytes
+    assert f(16, 32, 8, 4096, 128, 1024) == 1318912 + 512 * 16
     assert E.attn_decode_workspace_bytes(1, 3, 2, 100, 64) == 0     # invalid sizes
     assert E.attn_decode_workspace_bytes(1, 2, 1, 100, 96) == 0
     assert E.attn_decode_workspace_bytes(0, 2, 1, 100, 64) == 0

@@ -81,6 +81,37 @@ def test_many_short_sequences(orc, kps):
     assert (o[sl.numpy() == 0] == 0).all() and np.isneginf(lse[sl.numpy() == 0]).all()
 
 
+@pytest.mark.parametrize("B,hi,kps", [(65, 30, 0), (577, 24, 0), (1100, 16, 5), (3000, 8, 0), (2000, 12, 1)])
+def test_large_batches(orc, B, hi, kps):
+    """Batches past one page of 64 sequence lengths.  The split kernel loads
+    the other pages eight at a time, for the batch total and again to find
+    each range's first key, so 577 and more sequences span several groups of
+    eight pages; empty sequences sit in every page, a whole page is empty,
+    and so is the last sequence.  keys_per_split = 1 gives 2048 ranges of a
+    few keys each."""
+    Hq, Hkv, d = 8, 2, 64
+    _, q, kc, vc = I.decode_inputs(B, Hq, Hkv, hi, d, "bf16", seed=90 + B)
+    g = torch.Generator().manual_seed(91 + B)
+    sl = torch.randint(0, hi + 1, (B,), generator=g, dtype=torch.int32)
+    sl[::11] = 0
+    sl[-1] = 0
+    if B >= 192:
+        sl[128:192] = 0
+    o, lse = _parity(orc, sl, q, kc, vc, 0.125, "%d sequences" % B, kps)
+    assert (o[sl.numpy() == 0] == 0).all() and np.isneginf(lse[sl.numpy() == 0]).all()
+
+
+def test_large_batch_paged(orc):
+    """A paged cache with 1500 sequences of up to 40 keys in blocks of 16."""
+    sl, q, kp, vp, bt = I.paged_decode_inputs(1500, 8, 2, 64, 16, 3, "bf16", seed=95, lo=0, hi=40, spare_blocks=3)
+    say("[paged] 1500 sequences, pool%s" % (tuple(kp.shape),))
+    o, lse = E.attn_decode_paged(dev(q), dev(kp), dev(vp), dev(bt), dev(sl), scale=0.125)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = orc.decode_paged(I.to_f64(q), I.to_f64(kp), I.to_f64(vp), bt.numpy(), sl.numpy(), 0.125)
+    assert_close("1500-sequence paged O", I.to_f64(o), o_ref, TOL_O["bf16"])
+    assert_close("1500-sequence paged LSE", I.to_f64(lse), lse_ref, TOL_LSE)
+
+
 def test_empty_cache_rejected():
     """max_seq_len = 0 (and B = 0) are invalid sizes: the call is refused
     before any launch and leaves o untouched."""
