@@ -531,6 +531,42 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(
 
     // ---- epilogue: O = u / l, LSE = ln(sum exp(s)) -----------------------
     const float l_tot = l_run + wave_xor32(l_run);
+    if constexpr (SK == 1) {
+        // Each lane holds 4-column pieces of its row, which would go out as
+        // 8-byte stores scattered over 32 rows.  Instead the wave writes its
+        // 32 rows to LDS (row-major, 16-byte chunks XOR-swizzled by row so the
+        // writes spread over the banks) and stores them back as whole rows:
+        // every wave-wide store covers 64 / CHK consecutive rows, 1 KB
+        // contiguous.  The K/V tiles are free once every wave has passed the
+        // barrier; wave w uses half w & 1 of buffer w / 2 (32 rows x D each).
+        constexpr int CHK = D / 8;  // 16-byte chunks per row
+        static_assert(NW <= 8 && 64 * D <= C::TILE, "four tile buffers hold 32 rows per wave");
+        __syncthreads();
+        __bf16 *stg = (wave_all < 2 ? sK0 : wave_all < 4 ? sK1 : wave_all < 6 ? sV0 : sV1) + (wave_all & 1) * 32 * D;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int chunk = cb * 4 + rr;  // columns 8 chunk .. + 7; this lane's half is 4 g .. + 3
+                const uint32_t lo = pack_bf16(acc[cb][4 * rr + 0] * inv, acc[cb][4 * rr + 1] * inv);
+                const uint32_t hi = pack_bf16(acc[cb][4 * rr + 2] * inv, acc[cb][4 * rr + 3] * inv);
+                *reinterpret_cast<u32x2 *>(stg + n * D + ((chunk ^ (n & (CHK - 1))) * 8) + 4 * g) = u32x2{lo, hi};
+            }
+        }
+        // a wave's LDS accesses complete in order, so its reads below see its writes
+        __bf16 *obase = O + ((size_t)(b * Hq + h) * Nq + prow) * D;
+        constexpr int RPI = 64 / CHK;  // rows per wave-wide store
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+            const int row = i * RPI + lane / CHK, chunk = lane % CHK;
+            const u32x4 val = *reinterpret_cast<const u32x4 *>(stg + row * D + ((chunk ^ (row & (CHK - 1))) * 8));
+            if (prow + row < Nq) *reinterpret_cast<u32x4 *>(obase + (size_t)row * D + chunk * 8) = val;
+        }
+        if (qi < Nq && LSE && g == 0)
+            LSE[(size_t)(b * Hq + h) * Nq + qi] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * LN2 : -INFINITY;
+        return;
+    }
     if (qi < Nq) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         __bf16 *orow = O + ((size_t)(b * Hq + h) * Nq + qi) * D;
