@@ -394,18 +394,34 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
         if (j + 1 < ntiles) tile(j + 1, sK1, sV1, sK0, sV0);
     }
 
-    // dQ = scale * acc; lane (n, g) holds columns cb*32 + 8 rr + 4 g + 0..3
-    if (qi < Nq) {
-        __bf16 *row = dQ + (qrow0 + qi) * D;
+    // dQ = scale * acc; lane (n, g) holds columns cb*32 + 8 rr + 4 g + 0..3.
+    // The wave writes its 32 rows to LDS (16-byte chunks XOR-swizzled by row)
+    // and stores them back as whole rows, 1 KB per wave-wide store, instead
+    // of 8-byte pieces over 32 rows.  The K/V tiles are free once every wave
+    // has passed the barrier; wave w uses half w & 1 of buffer w / 2.
+    {
+        constexpr int CHK = D / 8;  // 16-byte chunks per row
+        static_assert(NW <= 8 && 64 * D <= BN * D, "four tile buffers hold 32 rows per wave");
+        __syncthreads();
+        __bf16 *stg = (wave_s < 2 ? sK0 : wave_s < 4 ? sK1 : wave_s < 6 ? sV0 : sV1) + (wave_s & 1) * 32 * D;
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb) {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const int c = cb * 32 + 8 * rr + 4 * g;
+                const int chunk = cb * 4 + rr;
                 const uint32_t lo = pack_bf16(acc[cb][4 * rr + 0] * scale, acc[cb][4 * rr + 1] * scale);
                 const uint32_t hi = pack_bf16(acc[cb][4 * rr + 2] * scale, acc[cb][4 * rr + 3] * scale);
-                *reinterpret_cast<u32x2 *>(row + c) = u32x2{lo, hi};
+                *reinterpret_cast<u32x2 *>(stg + n * D + ((chunk ^ (n & (CHK - 1))) * 8) + 4 * g) = u32x2{lo, hi};
             }
+        }
+        // a wave's LDS accesses complete in order, so its reads below see its writes
+        __bf16 *obase = dQ + (qrow0 + prow) * D;
+        constexpr int RPI = 64 / CHK;  // rows per wave-wide store
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+            const int row = i * RPI + lane / CHK, chunk = lane % CHK;
+            const u32x4 val = *reinterpret_cast<const u32x4 *>(stg + row * D + ((chunk ^ (row & (CHK - 1))) * 8));
+            if (prow + row < Nq) *reinterpret_cast<u32x4 *>(obase + (size_t)row * D + chunk * 8) = val;
         }
     }
 }

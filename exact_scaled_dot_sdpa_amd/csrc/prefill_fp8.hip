@@ -365,23 +365,41 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_fp8_kernel(
     }
 
     // ---- epilogue ------------------------------------------------------------
+    // O goes out as whole rows: the wave writes its 32 bf16 rows to LDS
+    // (16-byte chunks XOR-swizzled by row), then stores them back with 1 KB
+    // wave-wide stores of consecutive rows, instead of 8-byte pieces over 32
+    // rows.  Once every wave has passed the barrier the fp8 tiles are free;
+    // wave w uses buffer w (32 rows x D bf16 = one tile's bytes).
     const float l_tot = l_run + wave_xor32(l_run);
-    if (qi < Nq) {
+    {
+        constexpr int CHK = D / 8;  // 16-byte chunks per row
+        static_assert(NTHR == 256 && 32 * D * 2 <= C::TILE8, "one fp8 tile buffer holds a wave's 32 rows");
+        __syncthreads();
+        __bf16 *stg = reinterpret_cast<__bf16 *>(wave_s == 0 ? sK0 : wave_s == 1 ? sK1 : wave_s == 2 ? sW0 : sW1);
         const float inv = l_tot > 0.f ? v_scale / l_tot : 0.f;
-        __bf16 *orow = O + ((size_t)(b * Hq + h) * Nq + qi) * D;
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb) {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const int c = cb * 32 + 8 * rr + 4 * g;
+                const int chunk = cb * 4 + rr;  // columns 8 chunk .. + 7; this lane's half is 4 g .. + 3
                 const uint32_t lo = pack_bf16(acc[cb][4 * rr + 0] * inv, acc[cb][4 * rr + 1] * inv);
                 const uint32_t hi = pack_bf16(acc[cb][4 * rr + 2] * inv, acc[cb][4 * rr + 3] * inv);
-                *reinterpret_cast<u32x2 *>(orow + c) = u32x2{lo, hi};
+                *reinterpret_cast<u32x2 *>(stg + n * D + ((chunk ^ (n & (CHK - 1))) * 8) + 4 * g) = u32x2{lo, hi};
             }
         }
-        if (LSE && g == 0)
-            LSE[(size_t)(b * Hq + h) * Nq + qi] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * LN2 : -INFINITY;
+        // a wave's LDS accesses complete in order, so its reads below see its writes
+        const int row0 = q0 + wave * 32;
+        __bf16 *obase = O + ((size_t)(b * Hq + h) * Nq + row0) * D;
+        constexpr int RPI = 64 / CHK;  // rows per wave-wide store
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+            const int row = i * RPI + lane / CHK, chunk = lane % CHK;
+            const u32x4 val = *reinterpret_cast<const u32x4 *>(stg + row * D + ((chunk ^ (row & (CHK - 1))) * 8));
+            if (row0 + row < Nq) *reinterpret_cast<u32x4 *>(obase + (size_t)row * D + chunk * 8) = val;
+        }
     }
+    if (qi < Nq && LSE && g == 0)
+        LSE[(size_t)(b * Hq + h) * Nq + qi] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * LN2 : -INFINITY;
 }
 
 template <int D, bool CAUSAL>
