@@ -489,6 +489,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(
     // 2^(m_side - m) and added (one more step of the online-softmax
     // recurrence, applied to two key ranges).  Lanes keep their layout, so
     // the merge is element-wise.
+    __bf16 *stage_sk = nullptr;  // key-split form: LDS this wave may reuse for its output rows
     if constexpr (SK > 1) {
         constexpr int NE = 16 * C::CB + 2;             // floats per lane
         constexpr int ARR_F = SK * C::TILE / 2;         // floats per LDS array
@@ -527,11 +528,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(
             }
             m_ref = mn;
         }
+        // only this wave reads its own staging blocks, so once its merge is
+        // done the first of them can hold its output rows
+        static_assert(NE * 64 * 4 >= 32 * D * 2, "a staging block holds 32 output rows");
+        stage_sk = reinterpret_cast<__bf16 *>(blk(wave_u) - lane);
     }
 
     // ---- epilogue: O = u / l, LSE = ln(sum exp(s)) -----------------------
     const float l_tot = l_run + wave_xor32(l_run);
-    if constexpr (SK == 1) {
+    {
         // Each lane holds 4-column pieces of its row, which would go out as
         // 8-byte stores scattered over 32 rows.  Instead the wave writes its
         // 32 rows to LDS (row-major, 16-byte chunks XOR-swizzled by row so the
@@ -539,10 +544,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(
         // every wave-wide store covers 64 / CHK consecutive rows, 1 KB
         // contiguous.  The K/V tiles are free once every wave has passed the
         // barrier; wave w uses half w & 1 of buffer w / 2 (32 rows x D each).
+        // The key-split form reuses the wave's own merge staging block.
         constexpr int CHK = D / 8;  // 16-byte chunks per row
         static_assert(NW <= 8 && 64 * D <= C::TILE, "four tile buffers hold 32 rows per wave");
-        __syncthreads();
-        __bf16 *stg = (wave_all < 2 ? sK0 : wave_all < 4 ? sK1 : wave_all < 6 ? sV0 : sV1) + (wave_all & 1) * 32 * D;
+        __bf16 *stg;
+        if constexpr (SK > 1) {
+            stg = stage_sk;
+        } else {
+            __syncthreads();
+            stg = (wave_all < 2 ? sK0 : wave_all < 4 ? sK1 : wave_all < 6 ? sV0 : sV1) + (wave_all & 1) * 32 * D;
+        }
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb) {
@@ -565,24 +576,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(
         }
         if (qi < Nq && LSE && g == 0)
             LSE[(size_t)(b * Hq + h) * Nq + qi] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * LN2 : -INFINITY;
-        return;
-    }
-    if (qi < Nq) {
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        __bf16 *orow = O + ((size_t)(b * Hq + h) * Nq + qi) * D;
-#pragma unroll
-        for (int cb = 0; cb < C::CB; ++cb) {
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int c = cb * 32 + 8 * rr + 4 * g;
-                const uint32_t lo = pack_bf16(acc[cb][4 * rr + 0] * inv, acc[cb][4 * rr + 1] * inv);
-                const uint32_t hi = pack_bf16(acc[cb][4 * rr + 2] * inv, acc[cb][4 * rr + 3] * inv);
-                *reinterpret_cast<u32x2 *>(orow + c) = u32x2{lo, hi};
-            }
-        }
-        if (LSE && g == 0)
-            LSE[(size_t)(b * Hq + h) * Nq + qi] =
-                l_tot > 0.f ? (m_ref + __log2f(l_tot)) * LN2 : -INFINITY;
     }
 }
 
